@@ -1,0 +1,100 @@
+// Shared device helpers for the gfx950 kernels: vector types, MFMA wrappers,
+// the 32x32 accumulator layout, bf16 packing and wave reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mapflow.h"
+
+namespace mf {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kMaxNB = 1024;        // key blocks per sequence
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kLdsPad = 16;         // bytes appended to every LDS row
+
+// ---------------------------------------------------------------------------
+// MFMA 32x32 tiles.
+//
+// Accumulator layout of every 32x32 MFMA on CDNA: lane l, register r holds
+//   C[m = 8 * (r / 4) + 4 * (l / 32) + (r % 4)][n = l % 32].
+// Operand layout: A lane l holds row m = l % 32, B lane l holds column
+// n = l % 32; the lanes of one half (l / 32) share their k-values.  Which
+// logical k each (half, element) carries is free as long as A and B agree,
+// so loaders below pick contiguous memory runs per lane.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int acc_row(int r, int lane) {
+  return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+}
+
+__device__ __forceinline__ f32x16 mfma_bf16(const bf16x8 a, const bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) z[r] = 0.f;
+  return z;
+}
+
+// bf16 helpers (bit patterns in uint32 pairs)
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  bf16x2 b = __builtin_convertvector(v, bf16x2);
+  return __builtin_bit_cast(uint32_t, b);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 w) { return __builtin_bit_cast(bf16x8, w); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Reductions over the 32 lanes of each wave half (lanes l and l ^ 32 are not mixed).
+__device__ __forceinline__ float half_sum(float v) {
+#pragma unroll
+  for (int o = 16; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
+
+// ---------------------------------------------------------------------------
+// Block-row table, built once per call from the device sequence offsets.
+// Global block-row gr -> (sequence, block index in the sequence), and a
+// schedule listing block-rows by block index descending (longest rows first).
+// ---------------------------------------------------------------------------
+struct RowInfo {
+  int32_t seq;
+  int32_t blk;      // I
+  int32_t start;    // first token of the sequence
+  int32_t len;      // sequence length
+};
+
+// Workspace carving with 256-byte alignment.
+struct Carve {
+  size_t off = 0;
+  template <typename T>
+  size_t take(size_t count) {
+    size_t o = (off + 255) & ~size_t(255);
+    off = o + count * sizeof(T);
+    return o;
+  }
+};
+
+}  // namespace mf

@@ -1,0 +1,261 @@
+// Dense causal attention for recomputed heads (MapFlow, "Accelerating
+// Cross-Model LLM Inference via Attention Map Reuse", §4: the receiver computes
+// its first layers normally) and the exact path a cache miss falls back to
+// (AttnCache guide, "AttnCache Guide: Reusing Attention Maps in LLM Prefill":
+// threshold-gated fallback to standard attention).
+//
+//   O_h = softmax(Q_h K_g^T / sqrt(d) + bias) V_g,  g = h / (Hq / Hkv), causal.
+//
+// One work-group per (query head, 64-row query block), one wave per 32 rows.
+// Key blocks stream through LDS; S^T tiles on MFMA leave each lane holding one
+// query row, so the running max and sum (online softmax) stay in the lane; the
+// probabilities, rounded to bf16, are already in the A-operand layout of the
+// P V product, which runs on MFMA against the transposed V tile.  No map is
+// stored.
+#include <type_traits>
+
+#include "mf_host.hpp"
+#include "mf_qk.hpp"
+
+namespace mf {
+
+constexpr int kDenseB = 64;
+
+template <int D, bool F32>
+struct DenseCfg {
+  static constexpr int B = kDenseB;
+  using C = QKCfg<B, D, F32>;
+  static constexpr int VPITCH = B * 2 + kLdsPad;
+  static constexpr int VBYTES = D * VPITCH;
+  static constexpr int VCPR = B * 2 / 16;
+  static constexpr int VNCH = D * VCPR / C::NT;
+  static constexpr int SMEM = C::KBYTES + VBYTES;
+  static_assert(VNCH * C::NT == D * VCPR, "V tile chunks must divide evenly");
+};
+
+template <int D, bool F32>
+__global__ __launch_bounds__(kDenseB * 2) void k_dense(
+    const void *__restrict__ qv, const void *__restrict__ kv, const uint16_t *__restrict__ vt,
+    int64_t T, int32_t Hq, int32_t grp, int32_t NBR, const RowInfo *__restrict__ rows,
+    const int32_t *__restrict__ sched, float scale2, BiasArgs bias, float *__restrict__ o) {
+  constexpr int B = kDenseB;
+  using DC = DenseCfg<D, F32>;
+  using C = typename DC::C;
+  using E = std::conditional_t<F32, float, uint16_t>;
+  __shared__ __attribute__((aligned(16))) char smem[DC::SMEM];
+  char *klds = smem;
+  char *vlds = smem + C::KBYTES;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m = lane & 31, hl = lane >> 5;
+  const int pos = blockIdx.x / Hq, h = blockIdx.x % Hq;
+  const int g = h / grp;
+  const int gr = sched[pos];
+  const RowInfo ri = rows[gr];
+  const int I = ri.blk, L = ri.len;
+  const int i_loc = wave * 32 + m;
+  const int i_pos = I * B + i_loc;
+  const bool rvalid = i_pos < L;
+  const int64_t tok0 = (int64_t)ri.start;
+  const int64_t tpad = (int64_t)NBR * B;
+
+  const E *qh = reinterpret_cast<const E *>(qv) + (int64_t)h * T * D;
+  const char *kh = reinterpret_cast<const char *>(kv) + (int64_t)g * T * D * C::ESZ;
+  const uint16_t *vtg = vt + (int64_t)g * D * tpad;
+  QOp<D, F32> qo;
+  load_q<D>(qo, rvalid ? qh + (tok0 + i_pos) * D : nullptr, hl);
+
+  auto gload_v = [&](u32x4 (&stg)[DC::VNCH], int J) {
+    const int64_t col0 = (int64_t)(gr - I + J) * B;
+#pragma unroll
+    for (int c = 0; c < DC::VNCH; ++c) {
+      const int idx = tid + c * C::NT;
+      const int d = idx / DC::VCPR, cc = idx % DC::VCPR;
+      stg[c] = *reinterpret_cast<const u32x4 *>(vtg + (int64_t)d * tpad + col0 + cc * 8);
+    }
+  };
+  auto lstore_v = [&](const u32x4 (&stg)[DC::VNCH]) {
+#pragma unroll
+    for (int c = 0; c < DC::VNCH; ++c) {
+      const int idx = tid + c * C::NT;
+      const int d = idx / DC::VCPR, cc = idx % DC::VCPR;
+      *reinterpret_cast<u32x4 *>(vlds + d * DC::VPITCH + cc * 16) = stg[c];
+    }
+  };
+
+  u32x4 kst[C::NCH];
+  u32x4 vst[DC::VNCH];
+  gload_tile<B, D, F32>(kst, kh, tok0, min(B, L), tid);
+  gload_v(vst, 0);
+  lstore_tile<B, D, F32>(klds, kst, tid);
+  lstore_v(vst);
+  __syncthreads();
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int nb = 0; nb < D / 32; ++nb) oacc[nb] = zero16();
+  float m_run = -INFINITY, l_run = 0.f;
+
+  for (int J = 0; J <= I; ++J) {
+    if (J < I) {
+      gload_tile<B, D, F32>(kst, kh, tok0 + (int64_t)(J + 1) * B, min(B, L - (J + 1) * B), tid);
+      gload_v(vst, J + 1);
+    }
+    f32x16 acc[B / 32];
+    st_tile<B, D>(acc, klds, qo, lane);
+    const bool plain = plain_tile(I, J, B, bias.sink_n, bias.sink2, bias.local_w, bias.local2);
+    float mx = logits_inplace<B>(acc, plain, rvalid, i_pos, J * B, scale2, bias.sink_n,
+                                 bias.sink2, bias.local_w, bias.local2, lane);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    const float m_new = fmaxf(m_run, mx);
+    const float msafe = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - msafe);
+    float rs = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < B / 32; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pv = rvalid ? fast_exp2(acc[mb][r] - msafe) : 0.f;
+        acc[mb][r] = pv;
+        rs += pv;
+      }
+    rs += __shfl_xor(rs, 32, kWave);
+    l_run = l_run * alpha + rs;
+    m_run = m_new;
+    // rescale accumulated rows: row acc_row(r) of this wave belongs to that lane
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float f = __shfl(alpha, acc_row(r, lane), kWave);
+#pragma unroll
+      for (int nb = 0; nb < D / 32; ++nb) oacc[nb][r] *= f;
+    }
+    // P (bf16, A operand) x V tile (LDS, B operand)
+#pragma unroll
+    for (int mb = 0; mb < B / 32; ++mb)
+#pragma unroll
+      for (int e2 = 0; e2 < 2; ++e2) {
+        u32x4 a;
+        a[0] = pack_bf16x2(acc[mb][8 * e2 + 0], acc[mb][8 * e2 + 1]);
+        a[1] = pack_bf16x2(acc[mb][8 * e2 + 2], acc[mb][8 * e2 + 3]);
+        a[2] = pack_bf16x2(acc[mb][8 * e2 + 4], acc[mb][8 * e2 + 5]);
+        a[3] = pack_bf16x2(acc[mb][8 * e2 + 6], acc[mb][8 * e2 + 7]);
+        const int j0 = mb * 32 + 16 * e2 + 4 * hl;
+#pragma unroll
+        for (int nb = 0; nb < D / 32; ++nb) {
+          const char *vp = vlds + (nb * 32 + m) * DC::VPITCH;
+          const uint2 lo = *reinterpret_cast<const uint2 *>(vp + j0 * 2);
+          const uint2 hi = *reinterpret_cast<const uint2 *>(vp + (j0 + 8) * 2);
+          const u32x4 b = u32x4{lo.x, lo.y, hi.x, hi.y};
+          oacc[nb] = mfma_bf16(as_bf16x8(a), as_bf16x8(b), oacc[nb]);
+        }
+      }
+    __syncthreads();
+    if (J < I) {
+      lstore_tile<B, D, F32>(klds, kst, tid);
+      lstore_v(vst);
+    }
+    __syncthreads();
+  }
+
+  float *oh = o + (int64_t)h * T * D;
+  const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = acc_row(r, lane);
+    const float f = __shfl(inv, row, kWave);
+    const int ip = I * B + wave * 32 + row;
+    if (ip < L) {
+      float *dst = oh + (tok0 + ip) * D + m;
+#pragma unroll
+      for (int nb = 0; nb < D / 32; ++nb) dst[nb * 32] = oacc[nb][r] * f;
+    }
+  }
+}
+
+// V [Hkv][T][D] -> Vt (same kernel shape as the apply path, block 64)
+template <int D>
+__global__ __launch_bounds__(256) void k_vtranspose64(const uint16_t *__restrict__ v, int64_t T,
+                                                      const RowInfo *__restrict__ rows,
+                                                      int32_t NBR, uint16_t *__restrict__ vt) {
+  constexpr int B = kDenseB, P = B + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t t[D * P];
+  const int gr = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+  const RowInfo ri = rows[gr];
+  const int nval = min(B, ri.len - ri.blk * B);
+  const int64_t tok0 = (int64_t)ri.start + (int64_t)ri.blk * B;
+  const uint16_t *src = v + ((int64_t)g * T + tok0) * D;
+  for (int idx = tid; idx < B * D / 8; idx += 256) {
+    const int j = idx / (D / 8), c = idx % (D / 8);
+    u32x4 x = u32x4{0u, 0u, 0u, 0u};
+    if (j < nval) x = *reinterpret_cast<const u32x4 *>(src + (int64_t)j * D + c * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      t[(c * 8 + 2 * e) * P + j] = (uint16_t)(x[e] & 0xffffu);
+      t[(c * 8 + 2 * e + 1) * P + j] = (uint16_t)(x[e] >> 16);
+    }
+  }
+  __syncthreads();
+  const int64_t tpad = (int64_t)NBR * B;
+  uint16_t *dst = vt + (int64_t)g * D * tpad + (int64_t)gr * B;
+  for (int idx = tid; idx < D * B / 8; idx += 256) {
+    const int d = idx / (B / 8), c = idx % (B / 8);
+    *reinterpret_cast<u32x4 *>(dst + (int64_t)d * tpad + c * 8) =
+        *reinterpret_cast<const u32x4 *>(&t[d * P + c * 8]);
+  }
+}
+
+template <int D, bool F32>
+static mf_status launch_dense(hipStream_t s, const void *q, const void *k, const void *v,
+                              int32_t Hq, int32_t Hkv, const SeqGeom &g, const BiasArgs &ba,
+                              float *o, void *ws, const VtWs &w) {
+  hipLaunchKernelGGL((k_vtranspose64<D>), dim3(g.NBR, Hkv), dim3(256), 0, s,
+                     reinterpret_cast<const uint16_t *>(v), g.T, at<RowInfo>(ws, w.rt.rows), g.NBR,
+                     at<uint16_t>(ws, w.vt));
+  if (hip_status() != MF_OK) return MF_ERR_HIP;
+  const float scale2 = kLog2e / sqrtf((float)D);
+  hipLaunchKernelGGL((k_dense<D, F32>), dim3((unsigned)((int64_t)g.NBR * Hq)), dim3(kDenseB * 2),
+                     0, s, q, k, at<uint16_t>(ws, w.vt), g.T, Hq, Hq / Hkv, g.NBR,
+                     at<RowInfo>(ws, w.rt.rows), at<int32_t>(ws, w.rt.sched), scale2, ba, o);
+  return hip_status();
+}
+
+}  // namespace mf
+
+using namespace mf;
+
+extern "C" size_t mf_dense_workspace_bytes(int32_t Hkv, const int32_t *cu, int32_t nseq,
+                                           int32_t d) {
+  SeqGeom g;
+  if (Hkv <= 0 || !valid_dim(d) || seq_geom(cu, nseq, kDenseB, &g) != MF_OK) return 0;
+  return vt_ws(g, Hkv, kDenseB, d).total;
+}
+
+extern "C" mf_status mf_dense_ref_attention(void *stream, const void *q, const void *k,
+                                            const void *v, mf_dtype qk_dtype, int32_t Hq,
+                                            int32_t Hkv, int32_t d, const int32_t *cu_host,
+                                            const int32_t *cu_dev, int32_t nseq,
+                                            const mf_logit_bias *bias, float *o, void *ws,
+                                            size_t ws_bytes) {
+  if (!cu_host || !cu_dev || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || !bias_ok(bias))
+    return MF_ERR_INVALID_ARG;
+  if (qk_dtype != MF_BF16 && qk_dtype != MF_FP32) return MF_ERR_UNSUPPORTED;
+  if (!valid_dim(d)) return MF_ERR_UNSUPPORTED;
+  SeqGeom g;
+  mf_status st = seq_geom(cu_host, nseq, kDenseB, &g);
+  if (st != MF_OK) return st;
+  if ((int64_t)g.NBR * Hq > INT32_MAX / 2) return MF_ERR_UNSUPPORTED;
+  if (g.T > 0 && (!q || !k || !v || !o)) return MF_ERR_INVALID_ARG;
+  const VtWs w = vt_ws(g, Hkv, kDenseB, d);
+  if (!ws || ws_bytes < w.total) return MF_ERR_WORKSPACE;
+  if (g.NBR == 0) return MF_OK;
+  void *wsa = reinterpret_cast<void *>((reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if ((st = launch_rowtable(s, cu_dev, g, kDenseB, wsa, w.rt)) != MF_OK) return st;
+  const BiasArgs ba = bias_args(bias);
+  const bool f32 = qk_dtype == MF_FP32;
+  if (d == 64)
+    return f32 ? launch_dense<64, true>(s, q, k, v, Hq, Hkv, g, ba, o, wsa, w)
+               : launch_dense<64, false>(s, q, k, v, Hq, Hkv, g, ba, o, wsa, w);
+  return f32 ? launch_dense<128, true>(s, q, k, v, Hq, Hkv, g, ba, o, wsa, w)
+             : launch_dense<128, false>(s, q, k, v, Hq, Hkv, g, ba, o, wsa, w);
+}

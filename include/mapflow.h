@@ -1,0 +1,209 @@
+/*
+ * mapflow.h — C ABI of the attention-map reuse library for MI355X (gfx950).
+ *
+ * Two halves of one data path, plus dense attention for recomputed heads:
+ *
+ *   mf_compress_topp        sender side: attention map of every source head,
+ *                           block-level top-p selection, kept blocks written as
+ *                           bf16 probability tiles in Block Sparse Row (BSR) form
+ *                           with per-row kept mass.
+ *                           MapFlow ("Accelerating Cross-Model LLM Inference via
+ *                           Attention Map Reuse"), §4 (top-p compression into
+ *                           BSR) and §5.2 (Attention State Compressor).
+ *   mf_apply_translated     receiver side: O_t = sum_h W[t,h] renorm(A_hat_h) V_g(t)
+ *                           for every target head, without a dense L x L map in
+ *                           device memory.  MapFlow §3.3 (linear head mapping),
+ *                           §5.4 (fused retrieval kernel).
+ *   mf_dense_ref_attention  softmax(Q K^T / sqrt(d) + bias) V, causal, for the
+ *                           receiver layers that are recomputed (MapFlow §4) and
+ *                           the exact path a cache miss falls back to (AttnCache
+ *                           guide, "AttnCache Guide: Reusing Attention Maps in
+ *                           LLM Prefill", threshold-gated fallback).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers are device pointers unless marked "host".  The caller owns all
+ *   memory; the library never allocates, frees or keeps a pointer after a call
+ *   returns.  Sizes of the caller-provided buffers come from the *_bytes /
+ *   *_max_tiles queries below.
+ * - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work is
+ *   enqueued asynchronously on it; no entry point synchronises except
+ *   mf_read_status.
+ * - Sequences are packed back to back along the token axis (variable-length
+ *   packing, MapFlow §6): sequence s occupies tokens [cu_seqlens[s],
+ *   cu_seqlens[s+1]).  Every call takes the same offsets twice: a host copy
+ *   (used to validate and size the launch) and a device copy (read by kernels);
+ *   they must hold the same values.
+ * - Tensors are head-major, head dimension innermost: Q, K [H][T][d], V
+ *   [Hkv][T][d], O [H][T][d] (fp32).  Key-block and query-block grids restart
+ *   at every sequence start.
+ * - Causal masking is per sequence: token i attends to keys j <= i of its own
+ *   sequence.  Logit offsets (mf_logit_bias) are added after the 1/sqrt(d)
+ *   scaling.
+ * - Argument errors are found on the host before anything is enqueued and
+ *   return MF_ERR_INVALID_ARG / MF_ERR_UNSUPPORTED / MF_ERR_WORKSPACE.  A
+ *   failed kernel launch returns MF_ERR_HIP.  A map that does not fit its
+ *   capacity is reported asynchronously through the map's device status word
+ *   (read with mf_read_status).
+ * - Results are deterministic: the same inputs give bitwise-identical maps and
+ *   outputs from run to run (fixed-order reductions, no floating-point atomics).
+ * - Supported: block B in {32, 64, 128}; head dim d in {64, 128}; at most 1024
+ *   key blocks per sequence; 0 < p <= 1; Ht % Hkv == 0 (and Hq % Hkv == 0).
+ * - Calls are thread-safe and keep no state between calls.
+ */
+#ifndef MAPFLOW_H
+#define MAPFLOW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mf_status {
+  MF_OK = 0,
+  MF_ERR_INVALID_ARG = 1,  /* bad pointer, size, offsets or threshold           */
+  MF_ERR_UNSUPPORTED = 2,  /* valid but not built: block, head dim, dtype, size */
+  MF_ERR_CAPACITY = 3,     /* (device status) more kept tiles than capacity     */
+  MF_ERR_HIP = 4,          /* a HIP launch or runtime call failed               */
+  MF_ERR_WORKSPACE = 5     /* workspace pointer NULL or smaller than required   */
+} mf_status;
+
+typedef enum mf_dtype { MF_BF16 = 0, MF_FP32 = 1 } mf_dtype;
+
+/* Logit offsets added after scaling: +sink_bias on key positions [0, sink_n) of
+ * each sequence, +local_bias where 0 <= i - j < local_w.  Both may apply.  A
+ * NULL pointer means no offsets. */
+typedef struct mf_logit_bias {
+  int32_t sink_n;
+  float sink_bias;
+  int32_t local_w;
+  float local_bias;
+} mf_logit_bias;
+
+/* Compressed map of Hs source heads in BSR form (MapFlow §4, §5.2).
+ *
+ * Row r = h * num_block_rows + global block-row, where global block-rows run
+ * over the sequences in order and, within a sequence, over its query blocks
+ * I = 0 .. ceil(L_s / B) - 1.  Row r holds the kept key blocks J <= I of that
+ * query block in ascending J: col_idx[row_ptr[r] .. row_ptr[r+1]).  Tile n is a
+ * full B x B row-major block of bf16 probabilities (round-to-nearest-even of the
+ * fp32 value exp(s_ij - lse_i), i.e. normalised over the whole causal row, not
+ * renormalised), zero above the diagonal and outside the sequence.
+ * kept_mass[h][token] is the sum, over the kept blocks of the token's row, of
+ * its unrounded probabilities.
+ *
+ * The caller allocates every array and sets the pointers and capacity_tiles;
+ * mf_compress_topp fills the four size fields and the arrays.  Apply only reads
+ * the map, so one map can serve any number of apply calls (MapFlow §5.2: one
+ * compressed map serves many receivers). */
+typedef struct mf_bsr_map {
+  int32_t num_heads;       /* Hs                                        (out) */
+  int32_t block;           /* B                                         (out) */
+  int32_t num_block_rows;  /* NBR = sum_s ceil(L_s / B)                 (out) */
+  int32_t total_tokens;    /* T = cu_seqlens[nseq]                      (out) */
+  int64_t capacity_tiles;  /* tiles/col_idx entries allocated            (in) */
+  int64_t *row_ptr;        /* [Hs * NBR + 1]                                  */
+  int32_t *col_idx;        /* [capacity_tiles]                                */
+  uint16_t *tiles;         /* [capacity_tiles][B][B] bf16 bit patterns        */
+  float *kept_mass;        /* [Hs][T]                                         */
+  int64_t *nnz;            /* device scalar: number of kept tiles             */
+  int32_t *status;         /* device scalar: MF_OK or MF_ERR_CAPACITY         */
+} mf_bsr_map;
+
+/* Number of global block-rows sum_s ceil(L_s / B); -1 if the offsets are invalid.
+ * cu_seqlens_host: host, nseq + 1 entries. */
+int32_t mf_num_block_rows(const int32_t *cu_seqlens_host, int32_t nseq, int32_t B);
+
+/* Worst-case kept tiles (every causal block): Hs * sum_s nb_s (nb_s + 1) / 2.
+ * -1 if the arguments are invalid.  A smaller capacity is allowed; overflow is
+ * reported through the map's status word and no tile beyond it is written. */
+int64_t mf_compress_max_tiles(int32_t Hs, const int32_t *cu_seqlens_host, int32_t nseq,
+                              int32_t B);
+
+/* Device workspace bytes mf_compress_topp needs (0 if the arguments are invalid).
+ * Holds per-(row, key block) log-sum-exp partials (4 bytes per causal query/key
+ * block pair and row), row normalisers, kept bitmaps and counts. */
+size_t mf_compress_workspace_bytes(int32_t Hs, const int32_t *cu_seqlens_host, int32_t nseq,
+                                   int32_t B, int32_t d);
+
+/* Sender-side compression (MapFlow §4, §5.2).
+ *
+ * q, k        [Hs][T][d], dtype qk_dtype (bf16 bit patterns or fp32).
+ * p           top-p threshold in (0, 1].  Each query-block row keeps the
+ *             shortest prefix of its causal key blocks, ordered by block mass
+ *             (sum of the block's probabilities) descending and lower block
+ *             index first on equal mass, whose cumulative mass reaches p times
+ *             the row's total.  p == 1 keeps every causal block.
+ * bias        host, may be NULL.
+ * map         host struct: pointers and capacity set by the caller; size fields
+ *             written here.
+ * workspace   device, at least mf_compress_workspace_bytes(...) bytes, 256-byte
+ *             aligned; contents are scratch and may be reused after the stream
+ *             has passed this call.
+ * Errors: MF_ERR_INVALID_ARG, MF_ERR_UNSUPPORTED, MF_ERR_WORKSPACE, MF_ERR_HIP. */
+mf_status mf_compress_topp(void *stream, const void *q, const void *k, mf_dtype qk_dtype,
+                           const int32_t *cu_seqlens_host, const int32_t *cu_seqlens_dev,
+                           int32_t nseq, int32_t Hs, int32_t d, int32_t B, double p,
+                           const mf_logit_bias *bias, mf_bsr_map *map, void *workspace,
+                           size_t workspace_bytes);
+
+/* Device workspace bytes mf_apply_translated needs: a block-padded, transposed
+ * copy of V ([Hkv][d][NBR * B] bf16) plus the block-row table.  0 if invalid. */
+size_t mf_apply_workspace_bytes(int32_t Hkv, const int32_t *cu_seqlens_host, int32_t nseq,
+                                int32_t B, int32_t d);
+
+/* Receiver-side translated retrieval (MapFlow §3.3, §5.4):
+ *   O_t[i,:] = sum_h W[t,h] sum_{J kept by h in i's row} sum_{j in J}
+ *              (A_hat_h[i,j] / kept_mass_h[i]) V_g(t)[j,:],   g(t) = t / (Ht / Hkv)
+ * With renorm == 0 the division by kept mass is dropped.  A row whose kept
+ * mass is 0 contributes nothing.  W = identity gives per-head reuse of the
+ * cached map (AttnCache guide, "Output = A_c @ V").
+ *
+ * map         host struct filled by mf_compress_topp; read only.
+ * W           [Ht][map->num_heads] fp32, any sign; zero entries are skipped.
+ * v           [Hkv][T][d] bf16 bit patterns, T = map->total_tokens.
+ * cu_seqlens  the offsets the map was built with.
+ * o           [Ht][T][d] fp32, fully overwritten.
+ * workspace   device, at least mf_apply_workspace_bytes(...) bytes.
+ * The map's status must be MF_OK (check with mf_read_status); a map that
+ * overflowed its capacity gives undefined output rows for the missing tiles.
+ * Errors: MF_ERR_INVALID_ARG, MF_ERR_UNSUPPORTED, MF_ERR_WORKSPACE, MF_ERR_HIP. */
+mf_status mf_apply_translated(void *stream, const mf_bsr_map *map, const float *W, int32_t Ht,
+                              const void *v, int32_t Hkv, int32_t d,
+                              const int32_t *cu_seqlens_host, const int32_t *cu_seqlens_dev,
+                              int32_t nseq, int32_t renorm, float *o, void *workspace,
+                              size_t workspace_bytes);
+
+/* Device workspace bytes mf_dense_ref_attention needs (transposed, block-padded
+ * V, as for apply, with B = 64).  0 if invalid. */
+size_t mf_dense_workspace_bytes(int32_t Hkv, const int32_t *cu_seqlens_host, int32_t nseq,
+                                int32_t d);
+
+/* Dense causal attention for recomputed heads (MapFlow §4; AttnCache guide,
+ * "The Quadratic Self-Attention Cost"):
+ *   O_h = softmax(Q_h K_g^T / sqrt(d) + bias) V_g,   g = h / (Hq / Hkv).
+ * q [Hq][T][d] and k [Hkv][T][d] in qk_dtype; v [Hkv][T][d] bf16; o [Hq][T][d]
+ * fp32.  No map is read or written.
+ * Errors: MF_ERR_INVALID_ARG, MF_ERR_UNSUPPORTED, MF_ERR_WORKSPACE, MF_ERR_HIP. */
+mf_status mf_dense_ref_attention(void *stream, const void *q, const void *k, const void *v,
+                                 mf_dtype qk_dtype, int32_t Hq, int32_t Hkv, int32_t d,
+                                 const int32_t *cu_seqlens_host, const int32_t *cu_seqlens_dev,
+                                 int32_t nseq, const mf_logit_bias *bias, float *o,
+                                 void *workspace, size_t workspace_bytes);
+
+/* Waits for `stream`, then returns the map's device status (MF_OK or
+ * MF_ERR_CAPACITY) and, if nnz_out is not NULL, stores the kept-tile count
+ * there (host).  The only call that synchronises.  MF_ERR_HIP if a HIP call
+ * failed. */
+mf_status mf_read_status(void *stream, const mf_bsr_map *map, int64_t *nnz_out);
+
+/* Static text for a status code. */
+const char *mf_status_string(mf_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAPFLOW_H */

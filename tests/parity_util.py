@@ -1,0 +1,156 @@
+"""Shared helpers of the GPU parity tests: move seeded inputs to the device, run
+the HIP path through the binding, and compare against the fp64 oracle.
+
+Comparison rules (floating point decides the kept sets, so they are compared up
+to the cut band; everything else to fixed tolerances):
+  kept sets   equal to the oracle's except blocks the oracle flags as
+              cut-ambiguous (mass within 1e-5 relative of the cut);
+  tiles       |bf16 tile - P| <= 2e-3 on blocks kept by both (bf16 rounding of a
+              probability <= 1 is at most 2^-9 ~ 1.95e-3 with nearest-even);
+  kept mass   1e-4 relative where the sets agree (fp32 sums of fp32 exponentials);
+  outputs     relative Frobenius error <= 1e-2 per (sequence, target head), over
+              the rows compared (bf16 tiles and bf16 mixed tiles feeding fp32
+              accumulation: per-element rounding 2^-9, averaged over a row).
+"""
+from __future__ import annotations
+
+import sys
+from typing import Dict, Iterable, List, Optional, Sequence, Tuple
+
+import numpy as np
+import torch
+
+from oracle import mapflow_oracle as orc
+from cross_model_sparse_amd import mapflow as mf
+
+TILE_ATOL = 2e-3
+KMASS_RTOL = 1e-4
+OUT_RFROB = 1e-2
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev_qk(wl, dev):
+    if wl.spec.qk_dtype == "bf16":
+        q = torch.from_numpy(wl.q_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+        k = torch.from_numpy(wl.k_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        q = torch.from_numpy(np.ascontiguousarray(wl.q)).to(dev)
+        k = torch.from_numpy(np.ascontiguousarray(wl.k)).to(dev)
+    return q, k
+
+
+def to_dev_v(wl, dev):
+    return torch.from_numpy(wl.v_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+def gpu_compress(wl, dev, p=None, capacity=None):
+    q, k = to_dev_qk(wl, dev)
+    m = mf.mf_compress_topp(q, k, wl.cu_seqlens, wl.spec.B, wl.spec.p if p is None else p,
+                            wl.bias(), capacity=capacity)
+    st, nnz = mf.mf_read_status(m)
+    return m, st, nnz
+
+
+class HostMap:
+    """CPU copy of the parts of a device map the checks need (selected rows only)."""
+
+    def __init__(self, m: "mf.BsrMap", rows: Optional[Sequence[int]] = None):
+        self.B = m.block
+        self.NBR = m.num_block_rows
+        self.row_ptr = m.row_ptr.cpu().numpy()
+        nnz = int(self.row_ptr[-1])
+        self.kept_mass = m.kept_mass.cpu().numpy()
+        if rows is None:
+            self.col_idx = m.col_idx[:nnz].cpu().numpy()
+            self.tiles = m.tiles[:nnz].float().cpu().numpy()
+            self.tile_base = 0
+            self.rows = None
+        else:
+            # gather only the requested BSR rows
+            idx = np.concatenate([np.arange(self.row_ptr[r], self.row_ptr[r + 1]) for r in rows])
+            it = torch.from_numpy(idx).to(m.col_idx.device)
+            self.sel_col = m.col_idx[it].cpu().numpy()
+            self.sel_tiles = m.tiles[it].float().cpu().numpy()
+            self.sel_pos = {}
+            o = 0
+            for r in rows:
+                n = int(self.row_ptr[r + 1] - self.row_ptr[r])
+                self.sel_pos[r] = (o, n)
+                o += n
+            self.rows = set(rows)
+
+    def row(self, r: int) -> Tuple[np.ndarray, np.ndarray]:
+        """(col_idx, tiles) of BSR row r."""
+        if self.rows is None:
+            a, b = self.row_ptr[r], self.row_ptr[r + 1]
+            return self.col_idx[a:b], self.tiles[a:b]
+        o, n = self.sel_pos[r]
+        return self.sel_col[o:o + n], self.sel_tiles[o:o + n]
+
+
+def global_row(cu, B, s, I) -> int:
+    nb = [(int(cu[t + 1] - cu[t]) + B - 1) // B for t in range(len(cu) - 1)]
+    return sum(nb[:s]) + I
+
+
+def check_rows(hm: HostMap, res: Dict[Tuple[int, int, int], "orc.RowResult"], cu, T) -> dict:
+    """Compare kept sets, tiles and kept mass of every oracle row in `res`."""
+    B = hm.B
+    stats = dict(rows=0, ambiguous_rows=0, tile_err=0.0, kmass_err=0.0, flips=[])
+    for (h, s, I), rr in res.items():
+        gr = global_row(cu, B, s, I)
+        r = h * hm.NBR + gr
+        cols, tiles = hm.row(r)
+        gset, oset = [int(c) for c in cols], rr.kept
+        assert gset == sorted(gset), f"row {(h, s, I)} col_idx not ascending"
+        diff = set(gset) ^ set(oset)
+        assert diff <= rr.ambiguous, (f"row {(h, s, I)}: kept {gset} vs oracle {oset}, "
+                                      f"ambiguous {sorted(rr.ambiguous)}")
+        if diff:
+            stats["ambiguous_rows"] += 1
+            stats["flips"].append((h, s, I))
+        for c, J in enumerate(gset):
+            if J in oset:
+                e = float(np.max(np.abs(tiles[c] - rr.tile(J, B))))
+                stats["tile_err"] = max(stats["tile_err"], e)
+                assert e <= TILE_ATOL, f"tile {(h, s, I, J)} max error {e}"
+        if not diff:
+            a = int(cu[s]) + I * B
+            km = hm.kept_mass[h, a:a + len(rr.rows)]
+            e = float(np.max(np.abs(km - rr.kmass) / rr.kmass))
+            stats["kmass_err"] = max(stats["kmass_err"], e)
+            assert e <= KMASS_RTOL, f"kept mass {(h, s, I)} rel error {e}"
+        stats["rows"] += 1
+    return stats
+
+
+def rel_frob(a: np.ndarray, b: np.ndarray) -> float:
+    den = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / (den if den > 0 else 1.0))
+
+
+def check_apply(O_gpu: np.ndarray, out: Dict[Tuple[int, int, int], np.ndarray], cu, B,
+                skip: Iterable[Tuple[int, int]] = ()) -> float:
+    """Relative Frobenius error per (sequence, target) over the compared block-rows.
+    O_gpu: [Ht][T][d] host array, or {t: [T][d]}. `skip`: (s, I) block-rows whose source sets legitimately
+    differ from the oracle at an ambiguous cut."""
+    skip = set(skip)
+    per = {}
+    for (t, s, I), blk in out.items():
+        if (s, I) in skip:
+            continue
+        a = int(cu[s]) + I * B
+        g = O_gpu[t][a:a + blk.shape[0]]
+        per.setdefault((t, s), []).append((g, blk))
+    worst = 0.0
+    for key, pairs in per.items():
+        g = np.concatenate([x for x, _ in pairs])
+        o = np.concatenate([y for _, y in pairs])
+        e = rel_frob(g, o)
+        worst = max(worst, e)
+        assert e <= OUT_RFROB, f"output {key}: relative Frobenius error {e}"
+    return worst

@@ -1,0 +1,110 @@
+"""C-ABI boundary on the CPU: the library loads, exports every entry point that
+include/mapflow.h declares, answers size queries, and rejects invalid arguments
+before touching the GPU (no device calls are made here)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from cross_model_sparse_amd import mapflow as mf
+from cross_model_sparse_amd import workloads as wlmod
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mf.LIB_PATH):
+        from cross_model_sparse_amd import build
+        build.build()
+    return mf.load()
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "mapflow.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mf_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = header_functions()
+    assert len(names) == 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(mf.EXPORTS) == names
+
+
+def cu(lens):
+    c = np.zeros(len(lens) + 1, dtype=np.int32)
+    c[1:] = np.cumsum(lens)
+    return c
+
+
+def test_size_queries(lib):
+    lens = [300, 0, 1, 129, 4096]
+    c = cu(lens)
+    nb = [(L + 63) // 64 for L in lens]
+    assert mf.mf_num_block_rows(c, 64) == sum(nb)
+    assert mf.mf_compress_max_tiles(5, c, 64) == 5 * sum(n * (n + 1) // 2 for n in nb)
+    ws = mf.mf_compress_workspace_bytes(5, c, 64, 128)
+    # partials alone: 4 bytes per (row, causal block) and head
+    assert ws >= 5 * 64 * sum(n * (n + 1) // 2 for n in nb) * 4
+    assert mf.mf_apply_workspace_bytes(2, c, 64, 128) >= 2 * 128 * sum(nb) * 64 * 2
+    assert mf.mf_dense_workspace_bytes(2, c, 64) > 0
+    # invalid geometry
+    assert mf.mf_num_block_rows(c, 48) == -1
+    assert mf.mf_num_block_rows(np.array([0, 5, 3], dtype=np.int32), 64) == -1
+    assert mf.mf_num_block_rows(np.array([1, 5], dtype=np.int32), 64) == -1
+    assert mf.mf_compress_max_tiles(0, c, 64) == -1
+    assert mf.mf_compress_workspace_bytes(5, c, 64, 96) == 0
+    # more than 1024 key blocks in one sequence
+    assert mf.mf_num_block_rows(cu([32 * 1024 + 1]), 32) == -1
+
+
+def _compress(lib, c, Hs=2, d=64, B=32, p=0.9, dtype=0, mp=True, ws=1 << 40, bias=None):
+    m = mf.MfBsrMap(0, 0, 0, 0, 10, 8, 8, 8, 8, 8, 8)
+    fake = ctypes.c_void_p(16)
+    return lib.mf_compress_topp(None, fake, fake, dtype, c.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                fake, len(c) - 1, Hs, d, B, p, bias,
+                                ctypes.byref(m) if mp else None, fake, ws)
+
+
+def test_compress_rejects_bad_arguments(lib):
+    c = cu([100, 50])
+    assert _compress(lib, c, mp=False) == mf.MF_ERR_INVALID_ARG
+    assert _compress(lib, c, B=48) == mf.MF_ERR_UNSUPPORTED
+    assert _compress(lib, c, d=96) == mf.MF_ERR_UNSUPPORTED
+    assert _compress(lib, c, dtype=7) == mf.MF_ERR_UNSUPPORTED
+    for p in (0.0, -0.5, 1.0000001, float("nan")):
+        assert _compress(lib, c, p=p) == mf.MF_ERR_INVALID_ARG
+    assert _compress(lib, c, Hs=0) == mf.MF_ERR_INVALID_ARG
+    assert _compress(lib, np.array([0, 10, 5], dtype=np.int32)) == mf.MF_ERR_INVALID_ARG
+    assert _compress(lib, c, ws=100) == mf.MF_ERR_WORKSPACE
+    bad = mf.MfLogitBias(4, float("inf"), 8, 1.0)
+    assert _compress(lib, c, bias=ctypes.byref(bad)) == mf.MF_ERR_INVALID_ARG
+
+
+def test_apply_and_dense_reject_bad_arguments(lib):
+    c = cu([100])
+    fake = ctypes.c_void_p(16)
+    pc = c.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    m = mf.MfBsrMap(2, 32, 4, 100, 10, 8, 8, 8, 8, 8, 8)
+    f = lib.mf_apply_translated
+    assert f(None, ctypes.byref(m), fake, 4, fake, 3, 64, pc, fake, 1, 1, fake, fake, 1 << 40) == mf.MF_ERR_INVALID_ARG
+    assert f(None, ctypes.byref(m), fake, 4, fake, 2, 80, pc, fake, 1, 1, fake, fake, 1 << 40) == mf.MF_ERR_UNSUPPORTED
+    m.num_block_rows = 5  # does not match the offsets
+    assert f(None, ctypes.byref(m), fake, 4, fake, 2, 64, pc, fake, 1, 1, fake, fake, 1 << 40) == mf.MF_ERR_INVALID_ARG
+    m.num_block_rows = 4
+    assert f(None, ctypes.byref(m), fake, 4, fake, 2, 64, pc, fake, 1, 1, fake, fake, 10) == mf.MF_ERR_WORKSPACE
+    g = lib.mf_dense_ref_attention
+    assert g(None, fake, fake, fake, 0, 6, 4, 64, pc, fake, 1, None, fake, fake, 1 << 40) == mf.MF_ERR_INVALID_ARG
+    assert g(None, fake, fake, fake, 0, 4, 4, 64, pc, fake, 1, None, fake, fake, 10) == mf.MF_ERR_WORKSPACE
+    assert lib.mf_read_status(None, None, None) == mf.MF_ERR_INVALID_ARG
+
+
+def test_status_strings(lib):
+    for s in range(6):
+        assert lib.mf_status_string(s).decode() not in ("", "unknown status")
+    assert lib.mf_status_string(99).decode() == "unknown status"

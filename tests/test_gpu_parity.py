@@ -1,0 +1,240 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Small cases run the whole oracle; full-size workloads run the whole HIP path at
+the benchmark's launch configuration and compare sampled block-rows the oracle
+can compute one by one.  Comparison rules are in parity_util.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import mapflow_oracle as orc
+from cross_model_sparse_amd import mapflow as mf
+from cross_model_sparse_amd import workloads as wlmod
+from parity_util import (HostMap, check_apply, check_rows, gpu_compress, global_row, rel_frob, say,
+                         to_dev_qk, to_dev_v, OUT_RFROB)
+
+pytestmark = pytest.mark.gpu
+
+
+def full_case(wl, dev, p=None, W=None, renorm=True):
+    """Whole oracle vs whole HIP path on a small workload."""
+    B = wl.spec.B
+    p = wl.spec.p if p is None else p
+    W = wl.W if W is None else W
+    say(f"case {wl.spec.name} lens={wl.lens[:8]} Hs={wl.spec.Hs} p={p} B={B}")
+    m, st, nnz = gpu_compress(wl, dev, p=p)
+    assert st == mf.MF_OK
+    res = orc.compress(wl.q, wl.k, wl.cu_seqlens, B, p, wl.bias())
+    hm = HostMap(m)
+    rp, _ = orc.bsr_layout(res, wl.spec.Hs, wl.cu_seqlens, B)
+    assert (np.diff(hm.row_ptr) >= 1).all() and hm.row_ptr[0] == 0 and hm.row_ptr[-1] == nnz
+    stats = check_rows(hm, res, wl.cu_seqlens, wl.T)
+    if stats["ambiguous_rows"] == 0:
+        assert np.array_equal(hm.row_ptr, rp)
+    Wt = torch.from_numpy(np.ascontiguousarray(W, dtype=np.float32)).to(dev)
+    O = mf.mf_apply_translated(m, Wt, to_dev_v(wl, dev), wl.cu_seqlens, renorm=renorm)
+    out = orc.apply(res, W, wl.v, wl.cu_seqlens, B, wl.spec.Hkv, renorm=renorm)
+    skip = {(s, I) for (h, s, I) in stats["flips"]}
+    err = check_apply(O.cpu().numpy(), out, wl.cu_seqlens, B, skip)
+    say(f"  rows={stats['rows']} flips={stats['ambiguous_rows']} tile_err={stats['tile_err']:.2e} "
+        f"kmass_err={stats['kmass_err']:.2e} out_err={err:.2e} nnz={nnz}")
+    return m, res, O, stats
+
+
+def test_workload1_full(gpu):
+    """The tiny workload itself: fp32 Q/K (fp32 MFMA logits), B = 32, d = 64."""
+    full_case(wlmod.make_config(1), gpu)
+
+
+@pytest.mark.parametrize("idx,lens,kw", [
+    (2, [1000], dict(Hs=8, Ht=8, Hkv=8)),
+    (3, [777], dict(Hs=6, Ht=8, Hkv=2)),
+    (4, [1100], dict(Hs=8, Ht=16, Hkv=16)),
+    (5, [300, 520, 64, 1, 129, 0, 700], dict(Hs=4, Ht=4, Hkv=4)),
+])
+def test_small_variants(gpu, idx, lens, kw):
+    """Each workload's generator at oracle-sized lengths with ragged tails, an empty
+    and a one-token sequence (multi-turn), GQA and sparse Dirichlet W."""
+    full_case(wlmod.small_variant(idx, lens, **kw), gpu)
+
+
+@pytest.mark.parametrize("B,d,dt", [(32, 64, "fp32"), (32, 128, "bf16"), (64, 64, "bf16"),
+                                    (64, 128, "fp32"), (128, 64, "bf16"), (128, 128, "fp32")])
+def test_block_dim_dtype_grid(gpu, B, d, dt):
+    spec = wlmod.Spec(f"grid B={B} d={d} {dt}", (333, 200), 3, 4, 2, d, B, 0.85, dt, 48, "gauss",
+                      w_var=0.3, seed=100 + B + d)
+    full_case(wlmod.make_workload(spec), gpu)
+
+
+def test_p_one_identity_is_dense(gpu):
+    """p = 1 keeps every causal block; with W = I the retrieval equals dense causal
+    attention (oracle dense and the library's dense kernel)."""
+    wl = wlmod.small_variant(2, [700, 250], Hs=4, Ht=4, Hkv=4)
+    W = np.eye(4, dtype=np.float32)
+    m, res, O, _ = full_case(wl, gpu, p=1.0, W=W)
+    D = orc.dense_attention(wl.q, wl.k, wl.v, wl.cu_seqlens, wl.bias())
+    q, k = to_dev_qk(wl, gpu)
+    Od = mf.mf_dense_ref_attention(q, k, to_dev_v(wl, gpu), wl.cu_seqlens, wl.bias()).cpu().numpy()
+    Og = O.cpu().numpy()
+    for h in range(4):
+        for s, (a, L) in enumerate(orc.seqs(wl.cu_seqlens)):
+            assert rel_frob(Og[h, a:a + L], D[(h, s)]) <= OUT_RFROB
+            assert rel_frob(Od[h, a:a + L], D[(h, s)]) <= OUT_RFROB
+
+
+def test_p_tiny_keeps_argmax(gpu):
+    wl = wlmod.small_variant(2, [640], Hs=2, Ht=2, Hkv=2)
+    m, res, _, _ = full_case(wl, gpu, p=1e-6)
+    hm = HostMap(m)
+    for (h, s, I), rr in res.items():
+        cols, _ = hm.row(h * hm.NBR + I)
+        assert len(cols) == 1
+
+
+def test_zero_weight_row_and_no_renorm(gpu):
+    wl = wlmod.small_variant(3, [500], Hs=4, Ht=4, Hkv=2)
+    W = wl.W.copy()
+    W[1] = 0.0
+    m, res, O, _ = full_case(wl, gpu, W=W, renorm=False)
+    assert float(O[1].abs().max()) == 0.0
+
+
+def test_capacity_overflow_reported_and_bounded(gpu):
+    """Capacity below the kept count: the status word says so, and nothing is written
+    past the capacity (canary tiles and indices stay intact)."""
+    wl = wlmod.small_variant(2, [900], Hs=3, Ht=3, Hkv=3)
+    m0, st0, nnz = gpu_compress(wl, gpu)
+    cap = nnz // 2
+    B = wl.spec.B
+    big = mf.alloc_map(3, wl.cu_seqlens, B, gpu, capacity=cap + 16)
+    canary_t = torch.full((16, B, B), 7.0, dtype=torch.bfloat16, device=gpu)
+    big.tiles[cap:] = canary_t
+    big.col_idx[cap:] = -77
+    m = mf.BsrMap(big.num_heads, B, big.num_block_rows, big.total_tokens, big.row_ptr,
+                  big.col_idx[:cap], big.tiles, big.kept_mass, big.nnz, big.status)
+    q, k = to_dev_qk(wl, gpu)
+    say(f"capacity {cap} of {nnz}")
+    mf.mf_compress_topp(q, k, wl.cu_seqlens, B, wl.spec.p, wl.bias(), out=m)
+    st, nnz2 = mf.mf_read_status(m)
+    assert st == mf.MF_ERR_CAPACITY and nnz2 == nnz
+    assert torch.equal(big.tiles[cap:], canary_t)
+    assert int((big.col_idx[cap:] != -77).sum()) == 0
+    # the tiles that fit are the same as in an unconstrained run
+    assert torch.equal(big.tiles[:cap], m0.tiles[:cap])
+
+
+def test_deterministic(gpu):
+    wl = wlmod.small_variant(5, [900, 333, 1200], Hs=4, Ht=4, Hkv=4)
+    Wt = torch.from_numpy(wl.W).to(gpu)
+    v = to_dev_v(wl, gpu)
+    outs = []
+    for _ in range(2):
+        m, st, nnz = gpu_compress(wl, gpu)
+        O = mf.mf_apply_translated(m, Wt, v, wl.cu_seqlens)
+        torch.cuda.synchronize()
+        outs.append((m.row_ptr.clone(), m.col_idx[:nnz].clone(), m.tiles[:nnz].clone(),
+                     m.kept_mass.clone(), O.clone()))
+    for a, b in zip(*outs):
+        assert torch.equal(a.view(torch.uint8) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.uint8) if b.dtype == torch.bfloat16 else b)
+
+
+def test_multiturn_prefix_rows_bitwise(gpu):
+    """Block-rows wholly inside a sequence's copy of sequence 0's head produce the
+    same kept sets, tiles, kept mass and outputs bit for bit."""
+    wl = wlmod.small_variant(5, [700, 900, 1100, 400], Hs=4, Ht=4, Hkv=4)
+    B = wl.spec.B
+    m, st, nnz = gpu_compress(wl, gpu)
+    O = mf.mf_apply_translated(m, torch.from_numpy(wl.W).to(gpu), to_dev_v(wl, gpu), wl.cu_seqlens).cpu()
+    hm = HostMap(m)
+    n = 0
+    for s in range(1, 4):
+        for I in range(wl.prefix[s] // B):
+            for h in range(4):
+                c0, t0 = hm.row(h * hm.NBR + global_row(wl.cu_seqlens, B, 0, I))
+                c1, t1 = hm.row(h * hm.NBR + global_row(wl.cu_seqlens, B, s, I))
+                assert np.array_equal(c0, c1) and np.array_equal(t0, t1)
+            a0, a1 = int(wl.cu_seqlens[0]) + I * B, int(wl.cu_seqlens[s]) + I * B
+            assert torch.equal(O[:, a0:a0 + B], O[:, a1:a1 + B])
+            assert np.array_equal(hm.kept_mass[:, a0:a0 + B], hm.kept_mass[:, a1:a1 + B])
+            n += 1
+    assert n > 0
+
+
+def test_max_blocks_per_sequence(gpu):
+    """1024 key blocks in one sequence (L = 32768, B = 32): sampled rows."""
+    spec = wlmod.Spec("max blocks", (32768,), 1, 1, 1, 64, 32, 0.9, "bf16", 64, "gauss", w_var=1.0, seed=77)
+    wl = wlmod.make_workload(spec)
+    m, st, nnz = gpu_compress(wl, gpu)
+    assert st == mf.MF_OK
+    rows = [(0, 0), (0, 511), (0, 1023)]
+    res = orc.compress(wl.q, wl.k, wl.cu_seqlens, 32, 0.9, wl.bias(), rows=rows)
+    hm = HostMap(m, rows=[I for (_, I) in rows])
+    check_rows(hm, res, wl.cu_seqlens, wl.T)
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, sampled rows
+# ---------------------------------------------------------------------------
+
+SAMPLE_ROWS = {
+    2: [(0, 0), (0, 17), (0, 63)],
+    3: [(0, 0), (0, 100), (0, 255)],
+    4: [(0, 3), (0, 255)],
+    5: [(0, 0), (0, 20), (3, 0), (7, 30), (15, 10)],
+}
+
+
+@pytest.mark.parametrize("idx", [2, 3, 4, 5])
+def test_full_size_sampled(gpu, idx):
+    wl = wlmod.make_config(idx)
+    B, Hs = wl.spec.B, wl.spec.Hs
+    rows = []
+    for (s, I) in SAMPLE_ROWS[idx]:
+        nb = (wl.lens[s] + B - 1) // B
+        rows.append((s, min(I, nb - 1)))
+    if idx == 5:  # and the last block-row of the longest sequence
+        s = int(np.argmax(wl.lens))
+        rows.append((s, (wl.lens[s] + B - 1) // B - 1))
+    say(f"full workload {idx}: T={wl.T} Hs={Hs} Ht={wl.spec.Ht} rows={rows}")
+    m, st, nnz = gpu_compress(wl, gpu)
+    assert st == mf.MF_OK
+    Wt = torch.from_numpy(wl.W).to(gpu)
+    O = mf.mf_apply_translated(m, Wt, to_dev_v(wl, gpu), wl.cu_seqlens)
+    res = orc.compress(wl.q, wl.k, wl.cu_seqlens, B, wl.spec.p, wl.bias(), rows=rows)
+    brows = [h * m.num_block_rows + global_row(wl.cu_seqlens, B, s, I) for h in range(Hs) for (s, I) in rows]
+    hm = HostMap(m, rows=brows)
+    stats = check_rows(hm, res, wl.cu_seqlens, wl.T)
+    targets = [0, wl.spec.Ht // 3, wl.spec.Ht - 1]
+    out = orc.apply(res, wl.W, wl.v, wl.cu_seqlens, B, wl.spec.Hkv, targets=targets, rows=rows)
+    Og = {t: O[t].cpu().numpy() for t in targets}
+    skip = {(s, I) for (h, s, I) in stats["flips"]}
+    err = check_apply(Og, out, wl.cu_seqlens, B, skip)
+    say(f"  nnz={nnz} rows={stats['rows']} flips={stats['ambiguous_rows']} tile_err={stats['tile_err']:.2e} "
+        f"kmass_err={stats['kmass_err']:.2e} out_err={err:.2e}")
+
+
+# ---------------------------------------------------------------------------
+# dense attention
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("lens,Hq,Hkv,d,dt", [([256], 2, 2, 64, "fp32"), ([500, 0, 37], 8, 2, 128, "bf16"),
+                                             ([1000], 4, 4, 64, "bf16")])
+def test_dense_attention(gpu, lens, Hq, Hkv, d, dt):
+    spec = wlmod.Spec("dense", tuple(lens), Hq, Hq, Hkv, d, 64, 1.0, dt, 100, "gauss", w_var=1.0, seed=55)
+    wl = wlmod.make_workload(spec)
+    q, _ = to_dev_qk(wl, gpu)
+    # K from the first Hkv heads of the drawn K, so K and V share the head count
+    kk = wl.k[:Hkv].copy()
+    if dt == "bf16":
+        k = torch.from_numpy(wl.k_bits[:Hkv].copy().view(np.int16)).to(gpu).view(torch.bfloat16)
+    else:
+        k = torch.from_numpy(kk).to(gpu)
+    say(f"dense lens={lens} Hq={Hq} Hkv={Hkv} d={d} {dt}")
+    O = mf.mf_dense_ref_attention(q, k, to_dev_v(wl, gpu), wl.cu_seqlens, wl.bias()).cpu().numpy()
+    D = orc.dense_attention(wl.q, kk, wl.v, wl.cu_seqlens, wl.bias())
+    for (h, s), ref in D.items():
+        a, L = orc.seqs(wl.cu_seqlens)[s]
+        if L:
+            assert rel_frob(O[h, a:a + L], ref) <= OUT_RFROB
