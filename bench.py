@@ -1,0 +1,211 @@
+"""Benchmark: compressed-map prefill throughput on one MI355X.
+
+One step = one pass of the whole hot path over one batch: block top-p
+compression of every source head's causal attention map into BSR tiles
+(mf_compress_topp) followed by translated retrieval for every target head
+(mf_apply_translated).  Inputs are seeded synthetic tensors already resident in
+device memory; the map, workspaces and output are preallocated.
+
+Prints one JSON line (rank 0).  The default workload is the long-context one:
+one sequence of 32768 tokens, 32 source heads -> 64 target heads, d = 128,
+B = 128, p = 0.95, bf16 Q/K/V, each target mixing 4 sources (Dirichlet weights).
+
+  python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0    # dense bf16 MFMA
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "cross_model_sparse_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(kernel: str, workload: str):
+    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE for this
+    kernel, if recorded for the current kernel sources (else None)."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        rec = json.load(open(p))
+    except (OSError, ValueError):
+        return None
+    r = rec.get(kernel, {}).get(workload)
+    if not r or r.get("source_hash") != source_hash():
+        return None
+    return r.get("bytes_per_launch")
+
+
+def algorithmic_bytes(wl, nnz: int) -> dict:
+    s = wl.spec
+    T, NBR = wl.T, sum((L + s.B - 1) // s.B for L in wl.lens)
+    e_qk = 4 if s.qk_dtype == "fp32" else 2
+    meta = (s.Hs * NBR + 1) * 8 + s.Hs * T * 4          # row_ptr + kept mass
+    tiles = nnz * (s.B * s.B * 2 + 4)                    # bf16 tiles + col_idx
+    compress = 2 * s.Hs * T * s.d * e_qk + tiles + meta
+    apply = tiles + meta + s.Hkv * T * s.d * 2 + s.Ht * s.Hs * 4 + s.Ht * T * s.d * 4
+    return dict(compress=compress, apply=apply)
+
+
+def cpu_baseline(wl, rows):
+    """The fp64 oracle on a bounded sample of block-rows (all heads, all targets),
+    scaled to the whole workload by the share of causal key blocks the sample covers."""
+    from threadpoolctl import threadpool_info
+    from oracle import mapflow_oracle as orc
+    s = wl.spec
+    t0 = time.perf_counter()
+    res = orc.compress(wl.q, wl.k, wl.cu_seqlens, s.B, s.p, wl.bias(), rows=rows)
+    orc.apply(res, wl.W, wl.v, wl.cu_seqlens, s.B, s.Hkv, rows=rows)
+    dt = time.perf_counter() - t0
+    blocks_sample = sum(I + 1 for (_, I) in rows)
+    blocks_total = sum(n * (n + 1) // 2 for n in ((L + s.B - 1) // s.B for L in wl.lens))
+    full = dt * blocks_total / blocks_sample
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return dict(value=wl.T / full, unit="tokens/s", cores=int(threads), kind="oracle",
+                sample=(f"fp64 numpy oracle, compress + apply of block-rows {[I for _, I in rows]} "
+                        f"(all {s.Hs} source / {s.Ht} target heads) in {dt:.1f} s, scaled by "
+                        f"{blocks_total}/{blocks_sample} causal key blocks to the whole workload"))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=4, help="workload index (4: long context)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only: the hot path is measured on a single MI355X "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}); multi-GPU sharding is not built.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from cross_model_sparse_amd import mapflow as mf
+    from cross_model_sparse_amd import workloads as wlmod
+
+    mf.load()
+    dev = torch.device("cuda:0")
+    t0 = time.perf_counter()
+    wl = wlmod.make_config(args.config)
+    s = wl.spec
+    log(f"workload {args.config}: {s.name}; T={wl.T} generated in {time.perf_counter() - t0:.1f}s")
+
+    if s.qk_dtype == "bf16":
+        q = torch.from_numpy(wl.q_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+        k = torch.from_numpy(wl.k_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        q = torch.from_numpy(wl.q).to(dev)
+        k = torch.from_numpy(wl.k).to(dev)
+    v = torch.from_numpy(wl.v_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    W = torch.from_numpy(wl.W).to(dev)
+    cu = wl.cu_seqlens
+    cu_dev = torch.from_numpy(cu).to(dev)
+    m = mf.alloc_map(s.Hs, cu, s.B, dev)
+    ws_c = torch.empty(mf.mf_compress_workspace_bytes(s.Hs, cu, s.B, s.d), dtype=torch.uint8, device=dev)
+    ws_a = torch.empty(mf.mf_apply_workspace_bytes(s.Hkv, cu, s.B, s.d), dtype=torch.uint8, device=dev)
+    O = torch.empty((s.Ht, wl.T, s.d), dtype=torch.float32, device=dev)
+    bias = wl.bias()
+
+    def step():
+        mf.mf_compress_topp(q, k, cu, s.B, s.p, bias, out=m, workspace=ws_c, cu_dev=cu_dev)
+        mf.mf_apply_translated(m, W, v, cu, out=O, workspace=ws_a, cu_dev=cu_dev)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    nnz = None
+    if args.warmup > 0:
+        st, nnz = mf.mf_read_status(m)
+        if st != mf.MF_OK:
+            raise SystemExit(f"compression status {st}")
+        log(f"warmup done: nnz={nnz} tiles ({nnz / m.capacity:.3f} of causal)")
+
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        mf.mf_compress_topp(q, k, cu, s.B, s.p, bias, out=m, workspace=ws_c, cu_dev=cu_dev)
+        ev[i][1].record(stream)
+        mf.mf_apply_translated(m, W, v, cu, out=O, workspace=ws_a, cu_dev=cu_dev)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    st2, nnz2 = mf.mf_read_status(m)
+    if st2 != mf.MF_OK or (nnz is not None and nnz2 != nnz):
+        raise SystemExit(f"compression status {st2}, kept tiles {nnz2} (warmup {nnz})")
+    nnz = nnz2
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    t_comp = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    t_apply = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    log(f"ms/step {ms_step:.3f}  compress {t_comp:.3f} ms  apply {t_apply:.3f} ms")
+
+    ab = algorithmic_bytes(wl, nnz)
+    workload = f"workload{args.config}"
+    achieved = ab["apply"] / (t_apply * 1e-3) / 1e9
+    traffic = traffic_record("mf_apply_translated", workload)
+    roof = dict(kernel="mf_apply_translated (fused retrieval)", bound="hbm", achieved=round(achieved, 1),
+                peak=HBM_PEAK_GBS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
+                algorithmic_bytes=int(ab["apply"]), ms_per_launch=round(t_apply, 4),
+                compress_ms=round(t_comp, 4),
+                compress_gbs=round(ab["compress"] / (t_comp * 1e-3) / 1e9, 1))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        nb = (wl.lens[0] + s.B - 1) // s.B
+        rows = [(0, nb - 1), (0, nb // 2)]
+        log(f"cpu baseline on block-rows {rows} ...")
+        cpu = cpu_baseline(wl, rows)
+        log(f"cpu baseline {cpu['value']:.1f} tokens/s")
+
+    line = {
+        "metric": "compressed-map prefill tokens/s at L=32K (compress+apply)",
+        "value": round(wl.T / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if s.qk_dtype == "bf16" else "fp32",
+        "data": "synthetic",
+        "config": {"workload": s.name, "tokens": wl.T, "source_heads": s.Hs, "target_heads": s.Ht,
+                   "v_heads": s.Hkv, "head_dim": s.d, "block": s.B, "top_p": s.p,
+                   "kept_tiles": nnz, "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -25,6 +25,7 @@
 namespace mf {
 
 constexpr int kXcds = 8;
+constexpr int kBufferFlags = 0x00020000;  // buffer descriptor word 3 for raw dword loads
 
 // ---------------------------------------------------------------------------
 // V [Hkv][T][D] -> Vt [Hkv][D][NBR * B], zero past each sequence end
@@ -65,28 +66,43 @@ __global__ __launch_bounds__(256) void k_vtranspose(const uint16_t *__restrict__
 // ---------------------------------------------------------------------------
 template <int B, int D>
 struct ApplyCfg {
-  static constexpr int NW = B / 32;
-  static constexpr int NT = B * 2;
-  static constexpr int VPITCH = B * 2 + kLdsPad;  // bytes per Vt row (one value column)
+  static constexpr int NW = B / 16;                // waves per work-group, 16 rows each
+  static constexpr int NT = NW * 64;
+  static constexpr int KC = B / 32;                // 32-key chunks per key block
+  static constexpr int CPR = B * 2 / 16;           // 16-byte chunks per Vt row
+  static constexpr int VPITCH = B * 2;             // Vt row pitch in LDS (XOR-swizzled, no pad)
   static constexpr int VBYTES = D * VPITCH;
-  static constexpr int CPR = B * 2 / 16;
-  static constexpr int NCH = D * CPR / NT;
-  static_assert(NCH * NT == D * CPR, "V tile chunks must divide evenly");
+  static constexpr int VINST = VBYTES / 1024 / NW; // 1 KB direct loads per wave per tile
+  static_assert(VINST * 1024 * NW == VBYTES, "V tile must split into 1 KB wave loads");
 };
 
-// LDS after the V tile: src[Hs] int, wt[Hs] float, rbase[Hs] int64, bm[Hs][nbw],
-// pc[Hs][nbw], uni[nbw], coef[Hs][B], nsrc.
+// Dynamic LDS (byte offsets; the two V buffers are static): rbase[Hs] int64,
+// src[Hs], wt[Hs], bm[Hs][nbw], pc[Hs][nbw], uni[nbw], coef[Hs][B] (bf16 bits), nsrc.
 inline size_t apply_smem(int B, int D, int Hs, int nbw) {
-  size_t s = (size_t)D * (B * 2 + kLdsPad);
-  s += (size_t)Hs * (4 + 4 + 8);
+  (void)B;
+  (void)D;
+  size_t s = (size_t)Hs * (8 + 4 + 4);
   s += (size_t)Hs * nbw * 8 + (size_t)nbw * 4;
-  s += (size_t)Hs * B * 4;
+  s += (size_t)Hs * B * 2;
   s += 64;
   return s;
 }
 
-template <int B, int D>
-__global__ __launch_bounds__(B * 2) void k_apply(
+// acc += c * (bf16 pair) for both halves of a packed word, one dot2 each:
+// dot2([lo, hi], [c, 0]) = c * lo and dot2([lo, hi], [0, c]) = c * hi, fp32
+// accumulate; the coefficient is held in bf16.
+__device__ __forceinline__ void mix_word(float &even, float &odd, uint32_t w, uint32_t c_lo,
+                                         uint32_t c_hi) {
+  even = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w),
+                                         __builtin_bit_cast(bf16x2, c_lo), even, false);
+  odd = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w),
+                                        __builtin_bit_cast(bf16x2, c_hi), odd, false);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int B, int D, bool MANY>
+__global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(4))) void k_apply(
     const int64_t *__restrict__ row_ptr, const int32_t *__restrict__ col_idx,
     const uint16_t *__restrict__ tiles, const float *__restrict__ kept_mass, int32_t Hs,
     int32_t NBR, int64_t T, const float *__restrict__ W, int32_t Ht, int32_t grp,
@@ -94,22 +110,40 @@ __global__ __launch_bounds__(B * 2) void k_apply(
     const int32_t *__restrict__ sched, int32_t nbw, int64_t capacity, int32_t renorm,
     float *__restrict__ o) {
   using C = ApplyCfg<B, D>;
+  constexpr int KC = C::KC;
+  // The two V buffers are separate arrays so the compiler can tell that the
+  // direct loads into one never alias reads of the other (otherwise every LDS
+  // read waits for all outstanding direct loads).
+  __shared__ __attribute__((aligned(16))) char vA[C::VBYTES];
+  __shared__ __attribute__((aligned(16))) char vB[C::VBYTES];
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  char *vlds = smem;
-  int32_t *src = reinterpret_cast<int32_t *>(smem + C::VBYTES);
-  float *wt = reinterpret_cast<float *>(src + Hs);
-  int64_t *rbase = reinterpret_cast<int64_t *>(
-      (reinterpret_cast<uintptr_t>(wt + Hs) + 7) & ~uintptr_t(7));
-  uint32_t *bm = reinterpret_cast<uint32_t *>(rbase + Hs);
-  int32_t *pc = reinterpret_cast<int32_t *>(bm + Hs * nbw);
-  uint32_t *uni = reinterpret_cast<uint32_t *>(pc + Hs * nbw);
-  float *coef = reinterpret_cast<float *>(uni + nbw);
-  int32_t *nsrc_p = reinterpret_cast<int32_t *>(coef + Hs * B);
+  // byte offsets, kept relative to smem so every access stays an LDS access
+  const int o_rbase = 0;
+  const int o_src = o_rbase + Hs * 8;
+  const int o_wt = o_src + Hs * 4;
+  const int o_bm = o_wt + Hs * 4;
+  const int o_pc = o_bm + Hs * nbw * 4;
+  const int o_uni = o_pc + Hs * nbw * 4;
+  const int o_coef = o_uni + nbw * 4;
+  const int o_ns = (o_coef + Hs * B * 2 + 3) & ~3;
+  int64_t *rbase = reinterpret_cast<int64_t *>(smem + o_rbase);
+  int32_t *src = reinterpret_cast<int32_t *>(smem + o_src);
+  float *wt = reinterpret_cast<float *>(smem + o_wt);
+  uint32_t *bm = reinterpret_cast<uint32_t *>(smem + o_bm);
+  int32_t *pc = reinterpret_cast<int32_t *>(smem + o_pc);
+  uint32_t *uni = reinterpret_cast<uint32_t *>(smem + o_uni);
+  uint16_t *coef = reinterpret_cast<uint16_t *>(smem + o_coef);  // bf16 bits
+  int32_t *nsrc_p = reinterpret_cast<int32_t *>(smem + o_ns);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int m = lane & 31, hl = lane >> 5;
+  const int m16 = lane & 15, kg = lane >> 4;
+  // work-group id -> (query block, target): consecutive ids land on XCDs in
+  // turn; XCD x takes every eighth query block of the longest-first order, all
+  // targets of one block before the next, zig-zagging between rounds so the
+  // XCDs stay in step and share V through the memory-side cache.
   const int x = blockIdx.x % kXcds, kx = blockIdx.x / kXcds;
-  const int pos = (kx / Ht) * kXcds + x, t = kx % Ht;
+  const int round = kx / Ht, t = kx % Ht;
+  const int pos = round * kXcds + ((round & 1) ? (kXcds - 1 - x) : x);
   if (pos >= NBR) return;
   const int gr = sched[pos];
   const RowInfo ri = rows[gr];
@@ -120,7 +154,7 @@ __global__ __launch_bounds__(B * 2) void k_apply(
   const int64_t tok0 = (int64_t)ri.start;
   const int64_t tpad = (int64_t)NBR * B;
 
-  // sources with a nonzero weight, in head order
+  // ---- per-row setup: sources, kept bitmaps, ranks, coefficients ----------
   if (tid == 0) {
     int ns = 0;
     for (int h = 0; h < Hs; ++h) {
@@ -136,7 +170,9 @@ __global__ __launch_bounds__(B * 2) void k_apply(
   }
   for (int i = tid; i < Hs * nbw; i += C::NT) bm[i] = 0u;
   __syncthreads();
-  const int ns = *nsrc_p;
+  const int ns = __builtin_amdgcn_readfirstlane(*nsrc_p);
+  // targets with at most four sources run in the <false> instance, the rest in <true>
+  if (MANY != (ns > 4)) return;
   for (int q = 0; q < ns; ++q) {
     // entries past the capacity of an overflowed map are treated as missing
     const int64_t b = rbase[q], e = min(row_ptr[(int64_t)src[q] * NBR + gr + 1], capacity);
@@ -157,7 +193,7 @@ __global__ __launch_bounds__(B * 2) void k_apply(
         c = wt[q];
       }
     }
-    coef[q * B + il] = c;
+    coef[q * B + il] = (uint16_t)pack_bf16x2(c, 0.f);
   }
   __syncthreads();
   for (int q = tid; q < ns; q += C::NT) {
@@ -174,111 +210,210 @@ __global__ __launch_bounds__(B * 2) void k_apply(
   }
   __syncthreads();
 
-  // first key block of the union (uniform scan)
+  // next key block of the union at or after `from` (uniform), -1 if none
   auto next_J = [&](int from) -> int {
+    if (from >= n) return -1;
     for (int w = from >> 5; w < nw_row; ++w) {
-      uint32_t bits = uni[w];
+      uint32_t bits = __builtin_amdgcn_readfirstlane(uni[w]);
       if (w == (from >> 5)) bits &= ~((1u << (from & 31)) - 1u);
       if (bits) return w * 32 + __ffs(bits) - 1;
     }
     return -1;
   };
+  // tile index of source q at key block J, or -1 (uniform)
+  auto tile_of = [&](int q, int J) -> int64_t {
+    const uint32_t word = __builtin_amdgcn_readfirstlane(bm[q * nbw + (J >> 5)]);
+    if (!((word >> (J & 31)) & 1u)) return -1;
+    const int rank = __builtin_amdgcn_readfirstlane(pc[q * nbw + (J >> 5)]) +
+                     __popc(word & ((1u << (J & 31)) - 1u));
+    const int64_t rb = rbase[q];
+    const int64_t ti = (int64_t)__builtin_amdgcn_readfirstlane((int)(rb & 0xffffffff)) +
+                       ((int64_t)__builtin_amdgcn_readfirstlane((int)(rb >> 32)) << 32) + rank;
+    return ti < capacity ? ti : -1;
+  };
 
-  const int i_loc = wave * 32 + m;
-  f32x16 acc[D / 32];
-#pragma unroll
-  for (int nb = 0; nb < D / 32; ++nb) acc[nb] = zero16();
-
+  // V tile of key block J -> LDS buffer with direct buffer->LDS loads (the same
+  // load class as the tile reads, so the compiler's wait counts stay exact);
+  // chunk c of row d is stored at chunk position c ^ (d % CPR).
   const uint16_t *vtg = vt + (int64_t)g * D * tpad;
-  auto gload_v = [&](u32x4 (&stg)[C::NCH], int J) {
-    const int64_t col0 = (int64_t)(gr - I + J) * B;  // block J of this sequence
+  auto dma_v = [&](char *dstbuf, int J) {
+    const int64_t col0 = (int64_t)(gr - I + J) * B;
 #pragma unroll
-    for (int c = 0; c < C::NCH; ++c) {
-      const int idx = tid + c * C::NT;
-      const int d = idx / C::CPR, cc = idx % C::CPR;
-      stg[c] = *reinterpret_cast<const u32x4 *>(vtg + (int64_t)d * tpad + col0 + cc * 8);
+    for (int i = 0; i < C::VINST; ++i) {
+      const int blk = wave * C::VINST + i;        // 1 KB block of the tile
+      const int d0 = blk * 64 / C::CPR;           // first row of the block
+      const int k = blk * 64 + lane;              // 16-byte chunk index
+      const int d = k / C::CPR, pp = k % C::CPR;
+      const int c = pp ^ (d % C::CPR);
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)(vtg + (int64_t)d0 * tpad + col0), 0, 0x7fffffff, kBufferFlags);
+      const int off = (int)(((int64_t)(d - d0) * tpad + c * 8) * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dstbuf + blk * 1024), 16, off, 0, 0, 0);
     }
   };
-  auto lstore_v = [&](const u32x4 (&stg)[C::NCH]) {
-#pragma unroll
-    for (int c = 0; c < C::NCH; ++c) {
-      const int idx = tid + c * C::NT;
-      const int d = idx / C::CPR, cc = idx % C::CPR;
-      *reinterpret_cast<u32x4 *>(vlds + d * C::VPITCH + cc * 16) = stg[c];
-    }
+  auto vread = [&](const char *vl, int d, int c) -> u32x4 {
+    return *reinterpret_cast<const u32x4 *>(vl + d * C::VPITCH + ((c ^ (d % C::CPR)) << 4));
   };
 
-  int J = next_J(0);
-  u32x4 stg[C::NCH];
-  if (J >= 0) {
-    gload_v(stg, J);
-    lstore_v(stg);
-  }
-  __syncthreads();
-  while (J >= 0) {
-    const int Jn = (J + 1 < n) ? next_J(J + 1) : -1;
-    if (Jn >= 0) gload_v(stg, Jn);
+  // lane row: wave * 16 + m16; keys of chunk kc: kc * 32 + 8 * kg + e
+  const int r0 = wave * 16 + m16;
+  // Tiles are stored in fragment order: the wave's 16 rows x 32 keys of chunk kc
+  // are one contiguous 1 KB block, lane l's 16 bytes at l * 16.
+  const int loff = wave * KC * 512 + lane * 8;  // lane offset inside a tile (elements)
+  const uint16_t *rowbase = tiles + loff;
+  f32x4 acc[D / 16];
+#pragma unroll
+  for (int nb = 0; nb < D / 16; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    float mix[B / 2];
+  // translated row chunk (bf16) times the staged V tile
+  auto finish_chunk = [&](float (&mix)[8], const char *vl, int kc) {
+    u32x4 a;
 #pragma unroll
-    for (int e = 0; e < B / 2; ++e) mix[e] = 0.f;
-    const int jw = J >> 5;
-    const uint32_t below = (1u << (J & 31)) - 1u;
-    for (int q = 0; q < ns; ++q) {
-      const uint32_t word = bm[q * nbw + jw];
-      if (!((word >> (J & 31)) & 1u)) continue;
-      const int64_t tix = rbase[q] + pc[q * nbw + jw] + __popc(word & below);
-      if (tix >= capacity) continue;
-      const uint16_t *tp = tiles + tix * (int64_t)(B * B) + (int64_t)i_loc * B + 16 * hl;
-      const float c = coef[q * B + i_loc];
+    for (int e = 0; e < 4; ++e) a[e] = pack_bf16x2(mix[2 * e], mix[2 * e + 1]);
 #pragma unroll
-      for (int kc = 0; kc < B / 32; ++kc) {
-        const u32x4 v0 = *reinterpret_cast<const u32x4 *>(tp + kc * 32);
-        const u32x4 v1 = *reinterpret_cast<const u32x4 *>(tp + kc * 32 + 8);
+    for (int nb = 0; nb < D / 16; ++nb) {
+      const u32x4 b = vread(vl, nb * 16 + m16, kc * 4 + kg);
+      acc[nb] = mfma16_bf16(as_bf16x8(a), as_bf16x8(b), acc[nb]);
+    }
+  };
+  auto mix_src = [&](float (&mix)[8], const u32x4 &v, uint32_t c) {
+    const uint32_t c_lo = c, c_hi = c << 16;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          mix[kc * 16 + 2 * e] += c * bf16lo(v0[e]);
-          mix[kc * 16 + 2 * e + 1] += c * bf16hi(v0[e]);
-          mix[kc * 16 + 8 + 2 * e] += c * bf16lo(v1[e]);
-          mix[kc * 16 + 8 + 2 * e + 1] += c * bf16hi(v1[e]);
+    for (int e = 0; e < 4; ++e) mix_word(mix[2 * e], mix[2 * e + 1], v[e], c_lo, c_hi);
+  };
+
+  // tile pointers and coefficients of the first four sources at key block J
+  // Tile reads go through buffer descriptors (uniform base in scalar registers,
+  // one shared lane offset).  A source without a tile at this key block gets a
+  // zero-length descriptor: its loads return zeros without touching memory.
+  const int voff = loff * 2;  // bytes
+  struct Src4 {
+    __amdgpu_buffer_rsrc_t r[4];
+    uint32_t c[4];
+  };
+  auto src4 = [&](Src4 &S, int J) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      int64_t ti = -1;
+      if (J >= 0 && u < ns) ti = tile_of(u, J);
+      S.r[u] = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)(tiles + (ti >= 0 ? ti : 0) * (int64_t)(B * B)), 0, ti >= 0 ? B * B * 2 : 0,
+          kBufferFlags);
+      S.c[u] = ti >= 0 ? (uint32_t)coef[u * B + r0] : 0u;
+    }
+  };
+  auto load4 = [&](u32x4 (&dst)[4], const Src4 &S, int kc) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) dst[u] = __builtin_amdgcn_raw_buffer_load_b128(S.r[u], voff, kc * 1024, 0);
+  };
+
+  int J = (ns > 0) ? next_J(0) : -1;
+  if (J >= 0) dma_v(vA, J);
+  if constexpr (!MANY) {
+    // at most four sources: one chunk of loads in flight ahead of the one
+    // being mixed, across key-block boundaries
+    Src4 Sc, Sn;
+    src4(Sc, J);
+    u32x4 ta[2][4];
+    load4(ta[0], Sc, 0);  // zero-length descriptors when J < 0
+    // one key block: mix + multiply from vl while V of the next block loads into vnext
+    auto block = [&](int Jc, int Jn, const char *vl, char *vnext) {
+      src4(Sn, Jn);
+      // Own V loads for this block have landed (vector-memory loads retire in
+      // issue order and only the four loads of the prefetched chunk are
+      // younger) and own LDS reads are done; then the work-group barrier.  No
+      // full fence here: it would also drain the prefetched chunk.
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0x0074);  // vmcnt(4) lgkmcnt(0)
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      dma_v(vnext, Jn >= 0 ? Jn : Jc);  // unconditional (keeps wait counts static)
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        // (unconditional: a missing next block has zero-length descriptors, so
+        // the wait counts stay static)
+        if (kc + 1 < KC)
+          load4(ta[(kc + 1) & 1], Sc, kc + 1);
+        else
+          load4(ta[KC & 1], Sn, 0);
+        // keep the prefetch ahead of this chunk's work (the scheduler would
+        // otherwise sink it next to its first use)
+        __builtin_amdgcn_sched_barrier(0);
+        float mix[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mix[e] = 0.f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) mix_src(mix, ta[kc & 1][u], Sc.c[u]);
+        finish_chunk(mix, vl, kc);
+      }
+      if constexpr (KC & 1) {
+        // odd chunk count: the next block's first chunk went to buffer 1
+#pragma unroll
+        for (int u = 0; u < 4; ++u) ta[0][u] = ta[1][u];
+      }
+      Sc = Sn;
+    };
+    // two blocks per trip so each one's V buffers are fixed arrays
+    while (J >= 0) {
+      int Jn = next_J(J + 1);
+      block(J, Jn, vA, vB);
+      J = Jn;
+      if (J < 0) break;
+      Jn = next_J(J + 1);
+      block(J, Jn, vB, vA);
+      J = Jn;
+    }
+  } else {
+    int buf = 0;
+    while (J >= 0) {
+      const int Jn = next_J(J + 1);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (Jn >= 0) dma_v(buf ? vA : vB, Jn);
+      const char *vl = buf ? vB : vA;
+      // many sources: chunk by chunk, four sources at a time
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        float mix[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mix[e] = 0.f;
+        for (int q0 = 0; q0 < ns; q0 += 4) {
+          u32x4 va[4];
+          uint32_t cl[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            cl[u] = 0u;
+            const int q = q0 + u;
+            if (q >= ns) continue;
+            const int64_t ti = tile_of(q, J);
+            if (ti < 0) continue;
+            va[u] = *reinterpret_cast<const u32x4 *>(rowbase + ti * (int64_t)(B * B) + kc * 512);
+            cl[u] = (uint32_t)coef[q * B + r0];
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (cl[u] != 0u) mix_src(mix, va[u], cl[u]);
         }
+        finish_chunk(mix, vl, kc);
       }
+      buf ^= 1;
+      J = Jn;
     }
-#pragma unroll
-    for (int kc = 0; kc < B / 32; ++kc) {
-      u32x4 a0, a1;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        a0[e] = pack_bf16x2(mix[kc * 16 + 2 * e], mix[kc * 16 + 2 * e + 1]);
-        a1[e] = pack_bf16x2(mix[kc * 16 + 8 + 2 * e], mix[kc * 16 + 8 + 2 * e + 1]);
-      }
-#pragma unroll
-      for (int nb = 0; nb < D / 32; ++nb) {
-        const char *vp = vlds + (nb * 32 + m) * C::VPITCH + (kc * 32 + 16 * hl) * 2;
-        const u32x4 b0 = *reinterpret_cast<const u32x4 *>(vp);
-        const u32x4 b1 = *reinterpret_cast<const u32x4 *>(vp + 16);
-        acc[nb] = mfma_bf16(as_bf16x8(a0), as_bf16x8(b0), acc[nb]);
-        acc[nb] = mfma_bf16(as_bf16x8(a1), as_bf16x8(b1), acc[nb]);
-      }
-    }
-    __syncthreads();
-    if (Jn >= 0) lstore_v(stg);
-    __syncthreads();
-    J = Jn;
   }
 
   float *ot = o + (int64_t)t * T * D;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int il = wave * 32 + acc_row(r, lane);
-    const int ip = I * B + il;
+  for (int r = 0; r < 4; ++r) {
+    const int ip = I * B + wave * 16 + 4 * kg + r;
     if (ip < L) {
-      float *dst = ot + (tok0 + ip) * D + m;
+      float *dst = ot + (tok0 + ip) * D + m16;
 #pragma unroll
-      for (int nb = 0; nb < D / 32; ++nb) dst[nb * 32] = acc[nb][r];
+      for (int nb = 0; nb < D / 16; ++nb) dst[nb * 16] = acc[nb][r];
     }
   }
 }
+
+
 
 template <int B, int D>
 static mf_status launch_apply(hipStream_t s, const mf_bsr_map *map, const float *W, int32_t Ht,
@@ -291,11 +426,21 @@ static mf_status launch_apply(hipStream_t s, const mf_bsr_map *map, const float 
                      reinterpret_cast<const uint16_t *>(v), g.T, at<RowInfo>(ws, w.rt.rows), g.NBR,
                      at<uint16_t>(ws, w.vt));
   if (hip_status() != MF_OK) return MF_ERR_HIP;
-  if (smem > 64 * 1024)
-    hipFuncSetAttribute(reinterpret_cast<const void *>(&k_apply<B, D>),
+  if (smem > 64 * 1024) {
+    hipFuncSetAttribute(reinterpret_cast<const void *>(&k_apply<B, D, false>),
                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    hipFuncSetAttribute(reinterpret_cast<const void *>(&k_apply<B, D, true>),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  }
   const int64_t npos = ((int64_t)g.NBR + kXcds - 1) / kXcds * kXcds;
-  hipLaunchKernelGGL((k_apply<B, D>), dim3((unsigned)(npos * Ht)), dim3(B * 2), smem, s,
+  // one launch per source-count class; a work-group whose target is of the other
+  // class returns right after reading its weight row
+  hipLaunchKernelGGL((k_apply<B, D, false>), dim3((unsigned)(npos * Ht)), dim3(B * 4), smem, s,
+                     map->row_ptr, map->col_idx, map->tiles, map->kept_mass, map->num_heads,
+                     g.NBR, g.T, W, Ht, Ht / Hkv, at<uint16_t>(ws, w.vt),
+                     at<RowInfo>(ws, w.rt.rows), at<int32_t>(ws, w.rt.sched), nbw, map->capacity_tiles, renorm, o);
+  if (hip_status() != MF_OK) return MF_ERR_HIP;
+  hipLaunchKernelGGL((k_apply<B, D, true>), dim3((unsigned)(npos * Ht)), dim3(B * 4), smem, s,
                      map->row_ptr, map->col_idx, map->tiles, map->kept_mass, map->num_heads,
                      g.NBR, g.T, W, Ht, Ht / Hkv, at<uint16_t>(ws, w.vt),
                      at<RowInfo>(ws, w.rt.rows), at<int32_t>(ws, w.rt.sched), nbw, map->capacity_tiles, renorm, o);

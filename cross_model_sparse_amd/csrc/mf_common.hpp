@@ -12,6 +12,7 @@ namespace mf {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -36,6 +37,13 @@ __device__ __forceinline__ int acc_row(int r, int lane) {
 
 __device__ __forceinline__ f32x16 mfma_bf16(const bf16x8 a, const bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16x16x32 bf16: A lane l holds row l % 16, B lane l column l % 16, the four
+// lane groups (l / 16) share k-values; accumulator lane l, register r holds
+//   C[4 * (l / 16) + r][l % 16].
+__device__ __forceinline__ f32x4 mfma16_bf16(const bf16x8 a, const bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {

@@ -15,8 +15,8 @@
 //   k_offsets  exclusive scan of kept counts -> row_ptr, nnz, capacity status.
 //   k_tiles    one work-group per (source head, query block): recomputes only
 //              the kept tiles, rounds exp2(x - lse2) to bf16 (nearest even),
-//              transposes through LDS and writes each B x B tile with
-//              coalesced 16-byte stores, plus col_idx.
+//              reorders them through LDS into fragment order (see mf_bsr_map)
+//              and writes each tile with coalesced 16-byte stores, plus col_idx.
 #include <type_traits>
 
 #include "mf_host.hpp"
@@ -347,10 +347,14 @@ __global__ __launch_bounds__(B * 2) void k_tiles(
       char *dst = reinterpret_cast<char *>(tiles + (base + c) * (int64_t)B * B);
 #pragma unroll
       for (int k = 0; k < TC::TCH; ++k) {
-        const int idx = tid + k * C::NT;
-        const int rr = idx / (B * 2 / 16), cc = idx % (B * 2 / 16);
-        *reinterpret_cast<u32x4 *>(dst + rr * B * 2 + cc * 16) =
-            *reinterpret_cast<const u32x4 *>(tlds + rr * TC::TPITCH + cc * 16);
+        // fragment order: 16-byte chunk q = (row group * KC + key chunk) * 64 + f
+        // holds row 16 * group + f % 16, keys 32 * chunk + 8 * (f / 16) .. + 8
+        const int q = tid + k * C::NT;
+        const int blk = q >> 6, f = q & 63;
+        const int rr = (blk / (B / 32)) * 16 + (f & 15);
+        const int c0 = (blk % (B / 32)) * 32 + 8 * (f >> 4);
+        *reinterpret_cast<u32x4 *>(dst + q * 16) =
+            *reinterpret_cast<const u32x4 *>(tlds + rr * TC::TPITCH + c0 * 2);
       }
     }
     __syncthreads();

@@ -88,9 +88,17 @@ typedef struct mf_logit_bias {
  * over the sequences in order and, within a sequence, over its query blocks
  * I = 0 .. ceil(L_s / B) - 1.  Row r holds the kept key blocks J <= I of that
  * query block in ascending J: col_idx[row_ptr[r] .. row_ptr[r+1]).  Tile n is a
- * full B x B row-major block of bf16 probabilities (round-to-nearest-even of the
- * fp32 value exp(s_ij - lse_i), i.e. normalised over the whole causal row, not
+ * full B x B block of bf16 probabilities (round-to-nearest-even of the fp32 value
+ * exp(s_ij - lse_i), i.e. normalised over the whole causal row, not
  * renormalised), zero above the diagonal and outside the sequence.
+ *
+ * Element order inside a tile ("fragment order", the operand order of the
+ * receiver's 16x16x32 matrix instructions, so each 1 KB piece is one
+ * contiguous load): the tile is cut into (B/16) x (B/32) pieces of 16 rows x 32
+ * keys; piece (g, k) is the (g * B/32 + k)-th 1 KB block; inside it, 16-byte
+ * chunk f holds row 16 g + (f % 16), keys 32 k + 8 (f / 16) .. + 7.  Element
+ * (i, j) of the tile is therefore at
+ *   ((i/16 * B/32 + j/32) * 64 + (j%32)/8 * 16 + i%16) * 8 + j%8.
  * kept_mass[h][token] is the sum, over the kept blocks of the token's row, of
  * its unrounded probabilities.
  *

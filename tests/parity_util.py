@@ -55,6 +55,17 @@ def gpu_compress(wl, dev, p=None, capacity=None):
     return m, st, nnz
 
 
+def tiles_to_rowmajor(t: np.ndarray) -> np.ndarray:
+    """[n, B, B] tiles as stored (fragment order, see include/mapflow.h) -> row-major."""
+    n, B = t.shape[0], t.shape[1]
+    KC = B // 32
+    flat = t.reshape(n, -1)
+    i = np.arange(B)[:, None]
+    j = np.arange(B)[None, :]
+    off = (((i // 16) * KC + j // 32) * 64 + ((j % 32) // 8) * 16 + i % 16) * 8 + j % 8
+    return flat[:, off]
+
+
 class HostMap:
     """CPU copy of the parts of a device map the checks need (selected rows only)."""
 
@@ -66,7 +77,7 @@ class HostMap:
         self.kept_mass = m.kept_mass.cpu().numpy()
         if rows is None:
             self.col_idx = m.col_idx[:nnz].cpu().numpy()
-            self.tiles = m.tiles[:nnz].float().cpu().numpy()
+            self.tiles = tiles_to_rowmajor(m.tiles[:nnz].float().cpu().numpy())
             self.tile_base = 0
             self.rows = None
         else:
@@ -74,7 +85,7 @@ class HostMap:
             idx = np.concatenate([np.arange(self.row_ptr[r], self.row_ptr[r + 1]) for r in rows])
             it = torch.from_numpy(idx).to(m.col_idx.device)
             self.sel_col = m.col_idx[it].cpu().numpy()
-            self.sel_tiles = m.tiles[it].float().cpu().numpy()
+            self.sel_tiles = tiles_to_rowmajor(m.tiles[it].float().cpu().numpy())
             self.sel_pos = {}
             o = 0
             for r in rows:
