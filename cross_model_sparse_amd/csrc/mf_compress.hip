@@ -40,7 +40,7 @@ struct SelectCfg {
 };
 
 template <int B, int D, bool F32>
-__global__ __launch_bounds__(B * 2) void k_select(
+__global__ __launch_bounds__(B * 2) __attribute__((amdgpu_waves_per_eu(F32 ? 1 : 2))) void k_select(
     const void *__restrict__ qv, const void *__restrict__ kv, int64_t T, int32_t Hs, int32_t NBR,
     const RowInfo *__restrict__ rows, const int32_t *__restrict__ sched,
     const int64_t *__restrict__ pbase, int64_t ptot, float scale2, BiasArgs bias, double p,
@@ -248,7 +248,7 @@ struct TilesCfg {
 };
 
 template <int B, int D, bool F32>
-__global__ __launch_bounds__(B * 2) void k_tiles(
+__global__ __launch_bounds__(B * 2) __attribute__((amdgpu_waves_per_eu(F32 ? 1 : 2))) void k_tiles(
     const void *__restrict__ qv, const void *__restrict__ kv, int64_t T, int32_t Hs, int32_t NBR,
     const RowInfo *__restrict__ rows, const int32_t *__restrict__ sched, float scale2,
     BiasArgs bias, const float *__restrict__ lse2_in, const uint32_t *__restrict__ bitmaps,

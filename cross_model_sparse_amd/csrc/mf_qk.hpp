@@ -100,16 +100,17 @@ __device__ __forceinline__ void st_tile(f32x16 (&acc)[B / 32], const char *klds,
                                         const QOp<D, false> &qo, int lane) {
   using C = QKCfg<B, D, false>;
   const int m = lane & 31, hl = lane >> 5;
+  const char *rowp = klds + m * C::PITCH + hl * D;  // D/2 bf16 = D bytes
 #pragma unroll
-  for (int mb = 0; mb < B / 32; ++mb) {
-    acc[mb] = zero16();
-    const char *rowp = klds + (mb * 32 + m) * C::PITCH + hl * D;  // D/2 bf16 = D bytes
+  for (int mb = 0; mb < B / 32; ++mb) acc[mb] = zero16();
+  // k-step outer, key groups inner: B/32 independent accumulation chains
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      u32x4 a = *reinterpret_cast<const u32x4 *>(rowp + ks * 16);
+  for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+    for (int mb = 0; mb < B / 32; ++mb) {
+      u32x4 a = *reinterpret_cast<const u32x4 *>(rowp + mb * 32 * C::PITCH + ks * 16);
       acc[mb] = mfma_bf16(as_bf16x8(a), as_bf16x8(qo.v[ks]), acc[mb]);
     }
-  }
 }
 
 template <int B, int D>
@@ -117,19 +118,19 @@ __device__ __forceinline__ void st_tile(f32x16 (&acc)[B / 32], const char *klds,
                                         const QOp<D, true> &qo, int lane) {
   using C = QKCfg<B, D, true>;
   const int m = lane & 31, hl = lane >> 5;
+  const char *rowp = klds + m * C::PITCH + hl * (D / 2) * 4;
 #pragma unroll
-  for (int mb = 0; mb < B / 32; ++mb) {
-    acc[mb] = zero16();
-    const char *rowp = klds + (mb * 32 + m) * C::PITCH + hl * (D / 2) * 4;
+  for (int mb = 0; mb < B / 32; ++mb) acc[mb] = zero16();
 #pragma unroll
-    for (int c = 0; c < D / 8; ++c) {
-      float4 a = *reinterpret_cast<const float4 *>(rowp + c * 16);
+  for (int c = 0; c < D / 8; ++c)
+#pragma unroll
+    for (int mb = 0; mb < B / 32; ++mb) {
+      float4 a = *reinterpret_cast<const float4 *>(rowp + mb * 32 * C::PITCH + c * 16);
       acc[mb] = mfma_f32(a.x, qo.v[4 * c + 0], acc[mb]);
       acc[mb] = mfma_f32(a.y, qo.v[4 * c + 1], acc[mb]);
       acc[mb] = mfma_f32(a.z, qo.v[4 * c + 2], acc[mb]);
       acc[mb] = mfma_f32(a.w, qo.v[4 * c + 3], acc[mb]);
     }
-  }
 }
 
 // Scaled logits (log2 units) with causal mask and offsets, in place.
