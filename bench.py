@@ -90,6 +90,19 @@ def cpu_baseline(wl, rows):
                         f"{blocks_total}/{blocks_sample} causal key blocks to the whole workload"))
 
 
+def copy_calibration(torch, nbytes: int = 1 << 30, reps: int = 3):
+    """A plain copy of known size: under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE its
+    counters give the scale between the counters and bytes actually moved."""
+    dev = torch.device("cuda:0")
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -97,6 +110,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=4, help="workload index (4: long context)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (HBM counter scale)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -106,6 +121,9 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
     from cross_model_sparse_amd import mapflow as mf
     from cross_model_sparse_amd import workloads as wlmod
 

@@ -62,30 +62,198 @@ __global__ __launch_bounds__(256) void k_vtranspose(const uint16_t *__restrict__
 }
 
 // ---------------------------------------------------------------------------
-// k_apply
+// per (target, query block) set-up shared by both apply kernels
 // ---------------------------------------------------------------------------
-template <int B, int D>
-struct ApplyCfg {
-  static constexpr int NW = B / 16;                // waves per work-group, 16 rows each
-  static constexpr int NT = NW * 64;
-  static constexpr int KC = B / 32;                // 32-key chunks per key block
-  static constexpr int CPR = B * 2 / 16;           // 16-byte chunks per Vt row
-  static constexpr int VPITCH = B * 2;             // Vt row pitch in LDS (XOR-swizzled, no pad)
-  static constexpr int VBYTES = D * VPITCH;
-  static constexpr int VINST = VBYTES / 1024 / NW; // 1 KB direct loads per wave per tile
-  static_assert(VINST * 1024 * NW == VBYTES, "V tile must split into 1 KB wave loads");
-};
-
-// Dynamic LDS (byte offsets; the two V buffers are static): rbase[Hs] int64,
+// Dynamic LDS (byte offsets; the V buffers are static): rbase[Hs] int64,
 // src[Hs], wt[Hs], bm[Hs][nbw], pc[Hs][nbw], uni[nbw], coef[Hs][B] (bf16 bits), nsrc.
-inline size_t apply_smem(int B, int D, int Hs, int nbw) {
-  (void)B;
-  (void)D;
+// k_apply4 appends the union's key-block list: blist[nbw * 32] int32 and
+// tix[nbw * 32][4] int32 (tile index of each of up to four sources, -1 if none).
+inline size_t apply_smem(int B, int Hs, int nbw) {
   size_t s = (size_t)Hs * (8 + 4 + 4);
   s += (size_t)Hs * nbw * 8 + (size_t)nbw * 4;
   s += (size_t)Hs * B * 2;
   s += 64;
+  s += (size_t)nbw * 32 * 5 * 4;
   return s;
+}
+
+// LDS views of one (target, query block)'s source maps
+struct RowMaps {
+  int64_t *rbase;   // first tile of each source's block-row
+  int32_t *src;     // source heads with a nonzero weight
+  float *wt;        // their weights
+  uint32_t *bm;     // kept bitmaps [source][nbw]
+  int32_t *pc;      // exclusive popcount prefix of bm (tile rank of each word)
+  uint32_t *uni;    // union of the kept bitmaps
+  uint16_t *coef;   // [source][B] row coefficients W[t,h] / kmass_h[i], bf16 bits
+  int32_t *nsrc;
+  int32_t *tix;     // [k][4] tile index of source u at the k-th union block, -1 if none
+  int32_t *blist;   // [k] the k-th key block of the union, ascending
+  int nbw;
+};
+
+// byte offsets, kept relative to smem so every access stays an LDS access
+__device__ __forceinline__ RowMaps row_maps(char *smem, int Hs, int nbw, int B) {
+  const int o_rbase = 0;
+  const int o_src = o_rbase + Hs * 8;
+  const int o_wt = o_src + Hs * 4;
+  const int o_bm = o_wt + Hs * 4;
+  const int o_pc = o_bm + Hs * nbw * 4;
+  const int o_uni = o_pc + Hs * nbw * 4;
+  const int o_coef = o_uni + nbw * 4;
+  const int o_ns = (o_coef + Hs * B * 2 + 3) & ~3;
+  const int o_tix = (o_ns + 4 + 15) & ~15;
+  const int o_blist = o_tix + nbw * 32 * 16;
+  RowMaps m;
+  m.rbase = reinterpret_cast<int64_t *>(smem + o_rbase);
+  m.src = reinterpret_cast<int32_t *>(smem + o_src);
+  m.wt = reinterpret_cast<float *>(smem + o_wt);
+  m.bm = reinterpret_cast<uint32_t *>(smem + o_bm);
+  m.pc = reinterpret_cast<int32_t *>(smem + o_pc);
+  m.uni = reinterpret_cast<uint32_t *>(smem + o_uni);
+  m.coef = reinterpret_cast<uint16_t *>(smem + o_coef);
+  m.nsrc = reinterpret_cast<int32_t *>(smem + o_ns);
+  m.tix = reinterpret_cast<int32_t *>(smem + o_tix);
+  m.blist = reinterpret_cast<int32_t *>(smem + o_blist);
+  m.nbw = nbw;
+  return m;
+}
+
+// Sources of target t (nonzero weights, ascending head order) and the start of
+// their tile runs at block-row gr; clears the bitmaps.  Returns the source count
+// (uniform).
+template <int NT>
+__device__ int row_sources(const RowMaps &m, const float *__restrict__ W, int t, int Hs,
+                           const int64_t *__restrict__ row_ptr, int NBR, int gr, int tid) {
+  if (tid == 0) {
+    int ns = 0;
+    for (int h = 0; h < Hs; ++h) {
+      const float w = W[(int64_t)t * Hs + h];
+      if (w != 0.f) {
+        m.src[ns] = h;
+        m.wt[ns] = w;
+        m.rbase[ns] = row_ptr[(int64_t)h * NBR + gr];
+        ++ns;
+      }
+    }
+    *m.nsrc = ns;
+  }
+  for (int i = tid; i < Hs * m.nbw; i += NT) m.bm[i] = 0u;
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(*m.nsrc);
+}
+
+// Kept bitmaps of the ns sources at block-row gr, their tile ranks, the union
+// bitmap and the per-row coefficients (bf16): W[t,h] / kmass_h[i] when
+// renormalising (0 where the kept mass is 0), else W[t,h]; rows past the
+// sequence end get 0.
+template <int B, int NT>
+__device__ void row_maps_fill(const RowMaps &m, int ns, const int64_t *__restrict__ row_ptr,
+                              const int32_t *__restrict__ col_idx, int64_t capacity,
+                              const float *__restrict__ kept_mass, int64_t T, int NBR, int gr,
+                              int64_t tok0, int I, int L, int nw_row, int renorm, int tid) {
+  for (int q = 0; q < ns; ++q) {
+    // entries past the capacity of an overflowed map are treated as missing
+    const int64_t b = m.rbase[q], e = min(row_ptr[(int64_t)m.src[q] * NBR + gr + 1], capacity);
+    for (int64_t idx = b + tid; idx < e; idx += NT) {
+      const int J = col_idx[idx];
+      atomicOr(&m.bm[q * m.nbw + (J >> 5)], 1u << (J & 31));
+    }
+  }
+  for (int idx = tid; idx < ns * B; idx += NT) {
+    const int q = idx / B, il = idx % B;
+    const int ip = I * B + il;
+    float c = 0.f;
+    if (ip < L) {
+      if (renorm) {
+        const float km = kept_mass[(int64_t)m.src[q] * T + tok0 + ip];
+        c = km > 0.f ? m.wt[q] / km : 0.f;
+      } else {
+        c = m.wt[q];
+      }
+    }
+    m.coef[q * B + il] = (uint16_t)pack_bf16x2(c, 0.f);
+  }
+  __syncthreads();
+  for (int q = tid; q < ns; q += NT) {
+    int run = 0;
+    for (int w = 0; w < nw_row; ++w) {
+      m.pc[q * m.nbw + w] = run;
+      run += __popc(m.bm[q * m.nbw + w]);
+    }
+  }
+  if (tid < nw_row) {
+    uint32_t u = 0u;
+    for (int q = 0; q < ns; ++q) u |= m.bm[q * m.nbw + tid];
+    m.uni[tid] = u;
+  }
+  __syncthreads();
+}
+
+// next key block of the union at or after `from` (uniform), -1 if none
+__device__ __forceinline__ int union_next(const RowMaps &m, int n, int from) {
+  if (from < 0 || from >= n) return -1;
+  const int nw_row = (n + 31) / 32;
+  for (int w = from >> 5; w < nw_row; ++w) {
+    uint32_t bits = __builtin_amdgcn_readfirstlane(m.uni[w]);
+    if (w == (from >> 5)) bits &= ~((1u << (from & 31)) - 1u);
+    if (bits) return w * 32 + __ffs(bits) - 1;
+  }
+  return -1;
+}
+
+// tile index of source q at key block J, or -1 (uniform)
+__device__ __forceinline__ int64_t tile_index(const RowMaps &m, int q, int J, int64_t capacity) {
+  const uint32_t word = __builtin_amdgcn_readfirstlane(m.bm[q * m.nbw + (J >> 5)]);
+  if (!((word >> (J & 31)) & 1u)) return -1;
+  const int rank = __builtin_amdgcn_readfirstlane(m.pc[q * m.nbw + (J >> 5)]) +
+                   __popc(word & ((1u << (J & 31)) - 1u));
+  const int64_t rb = m.rbase[q];
+  const int64_t ti = (int64_t)__builtin_amdgcn_readfirstlane((int)(rb & 0xffffffff)) +
+                     ((int64_t)__builtin_amdgcn_readfirstlane((int)(rb >> 32)) << 32) + rank;
+  return ti < capacity ? ti : -1;
+}
+
+// The union's key blocks in ascending order with the tile index of each of the
+// (at most four) sources at each block; returns the number of blocks (uniform).
+template <int NT>
+__device__ int build_block_list(const RowMaps &m, int ns, int n, int64_t capacity, int tid) {
+  const int nw_row = (n + 31) / 32;
+  for (int J = tid; J < n; J += NT) {
+    const uint32_t w = m.uni[J >> 5];
+    if (!((w >> (J & 31)) & 1u)) continue;
+    int k = __popc(w & ((1u << (J & 31)) - 1u));
+    for (int i = 0; i < (J >> 5); ++i) k += __popc(m.uni[i]);
+    m.blist[k] = J;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      int32_t ti = -1;
+      if (u < ns) {
+        const uint32_t word = m.bm[u * m.nbw + (J >> 5)];
+        if ((word >> (J & 31)) & 1u) {
+          const int64_t x = m.rbase[u] + m.pc[u * m.nbw + (J >> 5)] +
+                            __popc(word & ((1u << (J & 31)) - 1u));
+          if (x < capacity) ti = (int32_t)x;
+        }
+      }
+      m.tix[k * 4 + u] = ti;
+    }
+  }
+  int total = 0;
+  for (int i = 0; i < nw_row; ++i) total += __popc(m.uni[i]);
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(total);
+}
+
+// work-group id -> (schedule position, target): consecutive ids land on XCDs in
+// turn; XCD x takes every eighth query block of the longest-first order, all
+// targets of one block before the next, zig-zagging between rounds so the XCDs
+// stay in step and share V through the memory-side cache.
+__device__ __forceinline__ void xcd_map(int Ht, int &pos, int &t) {
+  const int x = blockIdx.x % kXcds, kx = blockIdx.x / kXcds;
+  const int round = kx / Ht;
+  t = kx % Ht;
+  pos = round * kXcds + ((round & 1) ? (kXcds - 1 - x) : x);
 }
 
 // acc += c * (bf16 pair) for both halves of a packed word, one dot2 each:
@@ -101,166 +269,316 @@ __device__ __forceinline__ void mix_word(float &even, float &odd, uint32_t w, ui
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int B, int D, bool MANY>
-__global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(4))) void k_apply(
+// V tile of key block J -> LDS buffer with direct buffer->LDS loads (the same
+// load class as the tile reads, so the compiler's wait counts stay exact); the
+// wave moves VINST 1 KB blocks.  16-byte chunk c of row d is stored at chunk
+// position c ^ (d % CPR), so the MFMA B-operand reads below are conflict-free.
+template <int B, int D, int VINST>
+__device__ __forceinline__ void dma_v_tile(char *dstbuf, const uint16_t *vtg, int64_t tpad,
+                                           int64_t col0, int wave, int lane) {
+  constexpr int CPR = B * 2 / 16;   // 16-byte chunks per row
+  constexpr int RPB = 64 / CPR;     // rows per 1 KB block
+  // the swizzle of a block's rows repeats every PER blocks: the lane part of
+  // the offset takes PER values, the row part d0 * tpad * 2 is uniform
+  constexpr int PER = CPR * CPR / 64 > 1 ? CPR * CPR / 64 : 1;
+  // one descriptor per tile; byte offsets d * tpad * 2 stay below 2^31 (checked
+  // by the host)
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(vtg + col0), 0, 0x7fffffff, kBufferFlags);
+  const int dl = lane / CPR, pp = lane % CPR;
+#pragma unroll
+  for (int i = 0; i < VINST; ++i) {
+    const int blk = wave * VINST + i;        // 1 KB block of the tile
+    const int d0 = blk * RPB;                // its first row
+    const int c = pp ^ ((d0 + dl) % CPR);    // swizzled chunk position
+    (void)PER;
+    const int voff = (dl * (int)tpad + c * 8) * 2;
+    const int soff = d0 * (int)tpad * 2;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dstbuf + blk * 1024), 16, voff, soff, 0, 0);
+  }
+}
+
+template <int B>
+__device__ __forceinline__ u32x4 v_frag(const char *vl, int d, int c) {
+  constexpr int CPR = B * 2 / 16;
+  return *reinterpret_cast<const u32x4 *>(vl + d * (B * 2) + ((c ^ (d % CPR)) << 4));
+}
+
+// ---------------------------------------------------------------------------
+// k_apply4: targets with at most four sources (the translated map of a
+// head-mapping row).  One work-group per (target, query block), one wave per
+// RG 16-row MFMA groups.  The union's key blocks and each source's tile index
+// there are listed once in LDS, so stepping to the next block is one broadcast
+// read.
+//
+// Tile chunks (32 keys x 16 rows, 1 KB, fragment order) stream through a
+// register ring of NR chunk slots, NR - 1 chunks ahead of the one being mixed,
+// across key-block boundaries; V tiles go straight to a double LDS buffer one
+// key block ahead.  Loads of sources without a tile at a key block (and past
+// the last block) use zero-length descriptors: they return zeros without
+// touching memory and keep the number of loads in flight static.
+// ---------------------------------------------------------------------------
+constexpr int cgcd(int a, int b) { return b == 0 ? a : cgcd(b, a % b); }
+
+template <int B, int D>
+struct Apply4Cfg {
+  static constexpr int RG = 1;                       // 16-row MFMA groups per wave
+  static constexpr int NW = B / (16 * RG);           // waves
+  static constexpr int NT = NW * 64;
+  static constexpr int KC = B / 32;                  // 32-key chunks per key block
+  static constexpr int VBYTES = D * B * 2;
+  static constexpr int VINST = VBYTES / 1024 / NW;   // 1 KB direct loads per wave per V tile
+  // Ring slots (chunks).  Two, i.e. one chunk ahead: about eight work-groups
+  // read every source tile at nearly the same time, and the L2 does not merge
+  // their concurrent misses.  Deeper prefetch makes all of them miss together
+  // (measured at L = 32K: L2 hit rate 54% with two slots, 12% with four, and
+  // twice the fabric traffic); 32-row waves with more slots lose the same way.
+  static constexpr int NR = 2;
+  static constexpr int LPC = 4 * RG;                 // tile loads per chunk: row groups x 4 sources
+  // key blocks per unrolled trip: ring slots and V buffers both return to their start
+  static constexpr int TB = (NR * 2 * KC / cgcd(NR, 2 * KC)) / KC;
+  // descriptor queue depth: blocks from the current one to the farthest prefetched
+  static constexpr int DQ = (KC - 1 + NR - 1) / KC + 1;
+  static_assert(VINST * 1024 * NW == VBYTES, "V tile must split into 1 KB wave loads");
+  static_assert(TB % 2 == 0 && (TB * KC) % NR == 0, "trip must close the ring and V buffers");
+  static_assert((NR - 1) * LPC + VINST <= 63, "vmcnt range");
+};
+
+
+template <int B, int D>
+__global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(4))) void k_apply4(
     const int64_t *__restrict__ row_ptr, const int32_t *__restrict__ col_idx,
     const uint16_t *__restrict__ tiles, const float *__restrict__ kept_mass, int32_t Hs,
     int32_t NBR, int64_t T, const float *__restrict__ W, int32_t Ht, int32_t grp,
     const uint16_t *__restrict__ vt, const RowInfo *__restrict__ rows,
     const int32_t *__restrict__ sched, int32_t nbw, int64_t capacity, int32_t renorm,
     float *__restrict__ o) {
-  using C = ApplyCfg<B, D>;
-  constexpr int KC = C::KC;
-  // The two V buffers are separate arrays so the compiler can tell that the
-  // direct loads into one never alias reads of the other (otherwise every LDS
-  // read waits for all outstanding direct loads).
+  using C = Apply4Cfg<B, D>;
+  constexpr int KC = C::KC, NR = C::NR, TB = C::TB, DQ = C::DQ;
+  // separate arrays, so the compiler can tell that direct loads into one never
+  // alias reads of the other
   __shared__ __attribute__((aligned(16))) char vA[C::VBYTES];
   __shared__ __attribute__((aligned(16))) char vB[C::VBYTES];
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  // byte offsets, kept relative to smem so every access stays an LDS access
-  const int o_rbase = 0;
-  const int o_src = o_rbase + Hs * 8;
-  const int o_wt = o_src + Hs * 4;
-  const int o_bm = o_wt + Hs * 4;
-  const int o_pc = o_bm + Hs * nbw * 4;
-  const int o_uni = o_pc + Hs * nbw * 4;
-  const int o_coef = o_uni + nbw * 4;
-  const int o_ns = (o_coef + Hs * B * 2 + 3) & ~3;
-  int64_t *rbase = reinterpret_cast<int64_t *>(smem + o_rbase);
-  int32_t *src = reinterpret_cast<int32_t *>(smem + o_src);
-  float *wt = reinterpret_cast<float *>(smem + o_wt);
-  uint32_t *bm = reinterpret_cast<uint32_t *>(smem + o_bm);
-  int32_t *pc = reinterpret_cast<int32_t *>(smem + o_pc);
-  uint32_t *uni = reinterpret_cast<uint32_t *>(smem + o_uni);
-  uint16_t *coef = reinterpret_cast<uint16_t *>(smem + o_coef);  // bf16 bits
-  int32_t *nsrc_p = reinterpret_cast<int32_t *>(smem + o_ns);
+  const RowMaps mp = row_maps(smem, Hs, nbw, B);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m16 = lane & 15, kg = lane >> 4;
-  // work-group id -> (query block, target): consecutive ids land on XCDs in
-  // turn; XCD x takes every eighth query block of the longest-first order, all
-  // targets of one block before the next, zig-zagging between rounds so the
-  // XCDs stay in step and share V through the memory-side cache.
-  const int x = blockIdx.x % kXcds, kx = blockIdx.x / kXcds;
-  const int round = kx / Ht, t = kx % Ht;
-  const int pos = round * kXcds + ((round & 1) ? (kXcds - 1 - x) : x);
+  int pos, t;
+  xcd_map(Ht, pos, t);
   if (pos >= NBR) return;
   const int gr = sched[pos];
   const RowInfo ri = rows[gr];
   const int I = ri.blk, L = ri.len;
   const int n = I + 1;
-  const int nw_row = (n + 31) / 32;
   const int g = t / grp;
   const int64_t tok0 = (int64_t)ri.start;
   const int64_t tpad = (int64_t)NBR * B;
 
-  // ---- per-row setup: sources, kept bitmaps, ranks, coefficients ----------
-  if (tid == 0) {
-    int ns = 0;
-    for (int h = 0; h < Hs; ++h) {
-      const float w = W[(int64_t)t * Hs + h];
-      if (w != 0.f) {
-        src[ns] = h;
-        wt[ns] = w;
-        rbase[ns] = row_ptr[(int64_t)h * NBR + gr];
-        ++ns;
-      }
-    }
-    *nsrc_p = ns;
-  }
-  for (int i = tid; i < Hs * nbw; i += C::NT) bm[i] = 0u;
-  __syncthreads();
-  const int ns = __builtin_amdgcn_readfirstlane(*nsrc_p);
-  // targets with at most four sources run in the <false> instance, the rest in <true>
-  if (MANY != (ns > 4)) return;
-  for (int q = 0; q < ns; ++q) {
-    // entries past the capacity of an overflowed map are treated as missing
-    const int64_t b = rbase[q], e = min(row_ptr[(int64_t)src[q] * NBR + gr + 1], capacity);
-    for (int64_t idx = b + tid; idx < e; idx += C::NT) {
-      const int J = col_idx[idx];
-      atomicOr(&bm[q * nbw + (J >> 5)], 1u << (J & 31));
-    }
-  }
-  for (int idx = tid; idx < ns * B; idx += C::NT) {
-    const int q = idx / B, il = idx % B;
-    const int ip = I * B + il;
-    float c = 0.f;
-    if (ip < L) {
-      if (renorm) {
-        const float km = kept_mass[(int64_t)src[q] * T + tok0 + ip];
-        c = km > 0.f ? wt[q] / km : 0.f;
-      } else {
-        c = wt[q];
-      }
-    }
-    coef[q * B + il] = (uint16_t)pack_bf16x2(c, 0.f);
-  }
-  __syncthreads();
-  for (int q = tid; q < ns; q += C::NT) {
-    int run = 0;
-    for (int w = 0; w < nw_row; ++w) {
-      pc[q * nbw + w] = run;
-      run += __popc(bm[q * nbw + w]);
-    }
-  }
-  if (tid < nw_row) {
-    uint32_t u = 0u;
-    for (int q = 0; q < ns; ++q) u |= bm[q * nbw + tid];
-    uni[tid] = u;
-  }
-  __syncthreads();
+  const int ns = row_sources<C::NT>(mp, W, t, Hs, row_ptr, NBR, gr, tid);
+  if (ns > 4) return;  // handled by k_apply_many
+  row_maps_fill<B, C::NT>(mp, ns, row_ptr, col_idx, capacity, kept_mass, T, NBR, gr, tok0, I, L,
+                          (n + 31) / 32, renorm, tid);
 
-  // next key block of the union at or after `from` (uniform), -1 if none
-  auto next_J = [&](int from) -> int {
-    if (from >= n) return -1;
-    for (int w = from >> 5; w < nw_row; ++w) {
-      uint32_t bits = __builtin_amdgcn_readfirstlane(uni[w]);
-      if (w == (from >> 5)) bits &= ~((1u << (from & 31)) - 1u);
-      if (bits) return w * 32 + __ffs(bits) - 1;
-    }
-    return -1;
+  // coefficients of this lane's two rows, [c, 0] and [0, c] bf16 pairs (zero
+  // for missing sources)
+  constexpr int RG = C::RG;
+  uint32_t clo[RG][4];
+#pragma unroll
+  for (int h = 0; h < RG; ++h)
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      clo[h][u] = u < ns ? (uint32_t)mp.coef[u * B + wave * 16 * RG + 16 * h + m16] : 0u;
+
+  const int nblk = build_block_list<C::NT>(mp, ns, n, capacity, tid);
+
+  // k-th block of the union (uniform), -1 past the end
+  auto blk_J = [&](int k) -> int {
+    return k < nblk ? __builtin_amdgcn_readfirstlane(mp.blist[k]) : -1;
   };
-  // tile index of source q at key block J, or -1 (uniform)
-  auto tile_of = [&](int q, int J) -> int64_t {
-    const uint32_t word = __builtin_amdgcn_readfirstlane(bm[q * nbw + (J >> 5)]);
-    if (!((word >> (J & 31)) & 1u)) return -1;
-    const int rank = __builtin_amdgcn_readfirstlane(pc[q * nbw + (J >> 5)]) +
-                     __popc(word & ((1u << (J & 31)) - 1u));
-    const int64_t rb = rbase[q];
-    const int64_t ti = (int64_t)__builtin_amdgcn_readfirstlane((int)(rb & 0xffffffff)) +
-                       ((int64_t)__builtin_amdgcn_readfirstlane((int)(rb >> 32)) << 32) + rank;
-    return ti < capacity ? ti : -1;
+  // tile descriptors of the k-th union block; zero-length for a source without
+  // a tile there and past the last block
+  struct Src4 {
+    __amdgpu_buffer_rsrc_t r[4];
+  };
+  auto src4 = [&](Src4 &S, int k) {
+    u32x4 ti4 = u32x4{~0u, ~0u, ~0u, ~0u};
+    if (k < nblk) ti4 = *reinterpret_cast<const u32x4 *>(mp.tix + k * 4);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int ti = __builtin_amdgcn_readfirstlane((int)ti4[u]);
+      S.r[u] = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)(tiles + (int64_t)(ti >= 0 ? ti : 0) * (B * B)), 0, ti >= 0 ? B * B * 2 : 0,
+          kBufferFlags);
+    }
+  };
+  // chunk kc of both row groups: the wave's 1 KB fragment blocks of row groups
+  // 2 * wave and 2 * wave + 1, lane l's 16 bytes at l * 16
+  const int voff = (RG * wave * KC * 64 + lane) * 16;
+  auto load_chunk = [&](u32x4 (&dst)[RG][4], const Src4 &S, int kc) {
+#pragma unroll
+    for (int h = 0; h < RG; ++h)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        dst[h][u] = __builtin_amdgcn_raw_buffer_load_b128(S.r[u], voff, (h * KC + kc) * 1024, 0);
   };
 
-  // V tile of key block J -> LDS buffer with direct buffer->LDS loads (the same
-  // load class as the tile reads, so the compiler's wait counts stay exact);
-  // chunk c of row d is stored at chunk position c ^ (d % CPR).
   const uint16_t *vtg = vt + (int64_t)g * D * tpad;
   auto dma_v = [&](char *dstbuf, int J) {
-    const int64_t col0 = (int64_t)(gr - I + J) * B;
-#pragma unroll
-    for (int i = 0; i < C::VINST; ++i) {
-      const int blk = wave * C::VINST + i;        // 1 KB block of the tile
-      const int d0 = blk * 64 / C::CPR;           // first row of the block
-      const int k = blk * 64 + lane;              // 16-byte chunk index
-      const int d = k / C::CPR, pp = k % C::CPR;
-      const int c = pp ^ (d % C::CPR);
-      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-          (void *)(vtg + (int64_t)d0 * tpad + col0), 0, 0x7fffffff, kBufferFlags);
-      const int off = (int)(((int64_t)(d - d0) * tpad + c * 8) * 2);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dstbuf + blk * 1024), 16, off, 0, 0, 0);
-    }
-  };
-  auto vread = [&](const char *vl, int d, int c) -> u32x4 {
-    return *reinterpret_cast<const u32x4 *>(vl + d * C::VPITCH + ((c ^ (d % C::CPR)) << 4));
+    dma_v_tile<B, D, C::VINST>(dstbuf, vtg, tpad, (int64_t)(gr - I + J) * B, wave, lane);
   };
 
-  // lane row: wave * 16 + m16; keys of chunk kc: kc * 32 + 8 * kg + e
+  f32x4 acc[RG][D / 16];
+#pragma unroll
+  for (int h = 0; h < RG; ++h)
+#pragma unroll
+    for (int nb = 0; nb < D / 16; ++nb) acc[h][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (nblk > 0) {
+    // queue of tile descriptors: S[k] for the (cur + k)-th union block
+    Src4 S[DQ];
+#pragma unroll
+    for (int k = 0; k < DQ; ++k) src4(S[k], k);
+    u32x4 ring[NR][RG][4];
+    // prologue: the first V tile and chunks 0 .. NR-2
+    dma_v(vA, blk_J(0));
+#pragma unroll
+    for (int p = 0; p < NR - 1; ++p) load_chunk(ring[p], S[p / KC], p % KC);
+    int cur = 0;  // list position of the block being multiplied
+    bool done = false;
+    while (!done) {
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) {
+        if (done) break;
+        const char *vcur = (tb & 1) ? vB : vA;
+        char *vnxt = (tb & 1) ? vA : vB;
+        const int Jc = blk_J(cur), Jn = blk_J(cur + 1);
+        // block start: this wave's part of V(Jc) has landed and its LDS reads of
+        // the previous block are done; then the work-group barrier.  The wait
+        // is a full drain: direct-to-LDS loads are not ordered with loads into
+        // registers, so no partial count proves that V has landed.  Besides V
+        // only this block's first chunk is in flight, and it is needed next.
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        dma_v(vnxt, Jn >= 0 ? Jn : Jc);  // unconditional: static wait counts
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          const int pc = tb * KC + kc;          // chunk position in the trip
+          const int pf = kc + NR - 1;           // prefetched chunk, relative to this block
+          load_chunk(ring[(pc + NR - 1) % NR], S[pf / KC], pf % KC);
+          // keep the prefetch ahead of this chunk's work (the scheduler would
+          // otherwise sink it next to its first use)
+          __builtin_amdgcn_sched_barrier(0);
+          const u32x4(&cr)[RG][4] = ring[pc % NR];
+          u32x4 a[RG];
+#pragma unroll
+          for (int h = 0; h < RG; ++h) {
+            float mx[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) mx[e] = 0.f;
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                mix_word(mx[2 * e], mx[2 * e + 1], cr[h][u][e], clo[h][u], clo[h][u] << 16);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a[h][e] = pack_bf16x2(mx[2 * e], mx[2 * e + 1]);
+          }
+#pragma unroll
+          for (int nb = 0; nb < D / 16; ++nb) {
+            const u32x4 bv = v_frag<B>(vcur, nb * 16 + m16, kc * 4 + kg);
+#pragma unroll
+            for (int h = 0; h < RG; ++h)
+              acc[h][nb] = mfma16_bf16(as_bf16x8(a[h]), as_bf16x8(bv), acc[h][nb]);
+          }
+        }
+        // advance the queue
+#pragma unroll
+        for (int k = 0; k + 1 < DQ; ++k) S[k] = S[k + 1];
+        src4(S[DQ - 1], cur + DQ);
+        ++cur;
+        done = cur >= nblk;
+      }
+    }
+    // drain the prefetches of blocks that do not exist before the wave ends
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+
+  float *ot = o + (int64_t)t * T * D;
+#pragma unroll
+  for (int h = 0; h < RG; ++h)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int ip = I * B + wave * 16 * RG + 16 * h + 4 * kg + r;
+      if (ip < L) {
+        float *dst = ot + (tok0 + ip) * D + m16;
+#pragma unroll
+        for (int nb = 0; nb < D / 16; ++nb) dst[nb * 16] = acc[h][nb][r];
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// k_apply_many: targets with more than four sources (dense head mixing).  One
+// work-group per (target, query block), one wave per 16 query rows; per key
+// block and 32-key chunk, the sources are mixed four at a time.
+// ---------------------------------------------------------------------------
+template <int B, int D>
+struct ApplyManyCfg {
+  static constexpr int NW = B / 16;                // waves per work-group, 16 rows each
+  static constexpr int NT = NW * 64;
+  static constexpr int KC = B / 32;                // 32-key chunks per key block
+  static constexpr int VBYTES = D * B * 2;
+  static constexpr int VINST = VBYTES / 1024 / NW; // 1 KB direct loads per wave per tile
+  static_assert(VINST * 1024 * NW == VBYTES, "V tile must split into 1 KB wave loads");
+};
+
+template <int B, int D>
+__global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(4))) void k_apply_many(
+    const int64_t *__restrict__ row_ptr, const int32_t *__restrict__ col_idx,
+    const uint16_t *__restrict__ tiles, const float *__restrict__ kept_mass, int32_t Hs,
+    int32_t NBR, int64_t T, const float *__restrict__ W, int32_t Ht, int32_t grp,
+    const uint16_t *__restrict__ vt, const RowInfo *__restrict__ rows,
+    const int32_t *__restrict__ sched, int32_t nbw, int64_t capacity, int32_t renorm,
+    float *__restrict__ o) {
+  using C = ApplyManyCfg<B, D>;
+  constexpr int KC = C::KC;
+  __shared__ __attribute__((aligned(16))) char vA[C::VBYTES];
+  __shared__ __attribute__((aligned(16))) char vB[C::VBYTES];
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const RowMaps mp = row_maps(smem, Hs, nbw, B);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m16 = lane & 15, kg = lane >> 4;
+  int pos, t;
+  xcd_map(Ht, pos, t);
+  if (pos >= NBR) return;
+  const int gr = sched[pos];
+  const RowInfo ri = rows[gr];
+  const int I = ri.blk, L = ri.len;
+  const int n = I + 1;
+  const int g = t / grp;
+  const int64_t tok0 = (int64_t)ri.start;
+  const int64_t tpad = (int64_t)NBR * B;
+
+  const int ns = row_sources<C::NT>(mp, W, t, Hs, row_ptr, NBR, gr, tid);
+  if (ns <= 4) return;  // handled by k_apply4
+  row_maps_fill<B, C::NT>(mp, ns, row_ptr, col_idx, capacity, kept_mass, T, NBR, gr, tok0, I, L,
+                          (n + 31) / 32, renorm, tid);
+  auto next_J = [&](int from) -> int { return union_next(mp, n, from); };
+  auto tile_of = [&](int q, int J) -> int64_t { return tile_index(mp, q, J, capacity); };
+  const uint16_t *vtg = vt + (int64_t)g * D * tpad;
+  auto dma_v = [&](char *dstbuf, int J) {
+    dma_v_tile<B, D, C::VINST>(dstbuf, vtg, tpad, (int64_t)(gr - I + J) * B, wave, lane);
+  };
+
+  // lane row: wave * 16 + m16; keys of chunk kc: kc * 32 + 8 * kg + e.  The
+  // wave's 16 rows x 32 keys of chunk kc are one contiguous 1 KB block of the
+  // fragment-ordered tile, lane l's 16 bytes at l * 16.
   const int r0 = wave * 16 + m16;
-  // Tiles are stored in fragment order: the wave's 16 rows x 32 keys of chunk kc
-  // are one contiguous 1 KB block, lane l's 16 bytes at l * 16.
-  const int loff = wave * KC * 512 + lane * 8;  // lane offset inside a tile (elements)
-  const uint16_t *rowbase = tiles + loff;
+  const uint16_t *rowbase = tiles + wave * KC * 512 + lane * 8;
   f32x4 acc[D / 16];
 #pragma unroll
   for (int nb = 0; nb < D / 16; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -272,7 +590,7 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(4))) void
     for (int e = 0; e < 4; ++e) a[e] = pack_bf16x2(mix[2 * e], mix[2 * e + 1]);
 #pragma unroll
     for (int nb = 0; nb < D / 16; ++nb) {
-      const u32x4 b = vread(vl, nb * 16 + m16, kc * 4 + kg);
+      const u32x4 b = v_frag<B>(vl, nb * 16 + m16, kc * 4 + kg);
       acc[nb] = mfma16_bf16(as_bf16x8(a), as_bf16x8(b), acc[nb]);
     }
   };
@@ -281,124 +599,44 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(4))) void
 #pragma unroll
     for (int e = 0; e < 4; ++e) mix_word(mix[2 * e], mix[2 * e + 1], v[e], c_lo, c_hi);
   };
+  const uint16_t *coef = mp.coef;
 
-  // tile pointers and coefficients of the first four sources at key block J
-  // Tile reads go through buffer descriptors (uniform base in scalar registers,
-  // one shared lane offset).  A source without a tile at this key block gets a
-  // zero-length descriptor: its loads return zeros without touching memory.
-  const int voff = loff * 2;  // bytes
-  struct Src4 {
-    __amdgpu_buffer_rsrc_t r[4];
-    uint32_t c[4];
-  };
-  auto src4 = [&](Src4 &S, int J) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      int64_t ti = -1;
-      if (J >= 0 && u < ns) ti = tile_of(u, J);
-      S.r[u] = __builtin_amdgcn_make_buffer_rsrc(
-          (void *)(tiles + (ti >= 0 ? ti : 0) * (int64_t)(B * B)), 0, ti >= 0 ? B * B * 2 : 0,
-          kBufferFlags);
-      S.c[u] = ti >= 0 ? (uint32_t)coef[u * B + r0] : 0u;
-    }
-  };
-  auto load4 = [&](u32x4 (&dst)[4], const Src4 &S, int kc) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) dst[u] = __builtin_amdgcn_raw_buffer_load_b128(S.r[u], voff, kc * 1024, 0);
-  };
-
-  int J = (ns > 0) ? next_J(0) : -1;
+  int J = next_J(0);
   if (J >= 0) dma_v(vA, J);
-  if constexpr (!MANY) {
-    // at most four sources: one chunk of loads in flight ahead of the one
-    // being mixed, across key-block boundaries
-    Src4 Sc, Sn;
-    src4(Sc, J);
-    u32x4 ta[2][4];
-    load4(ta[0], Sc, 0);  // zero-length descriptors when J < 0
-    // one key block: mix + multiply from vl while V of the next block loads into vnext
-    auto block = [&](int Jc, int Jn, const char *vl, char *vnext) {
-      src4(Sn, Jn);
-      // Own V loads for this block have landed (vector-memory loads retire in
-      // issue order and only the four loads of the prefetched chunk are
-      // younger) and own LDS reads are done; then the work-group barrier.  No
-      // full fence here: it would also drain the prefetched chunk.
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_waitcnt(0x0074);  // vmcnt(4) lgkmcnt(0)
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      dma_v(vnext, Jn >= 0 ? Jn : Jc);  // unconditional (keeps wait counts static)
+  int buf = 0;
+  while (J >= 0) {
+    const int Jn = next_J(J + 1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (Jn >= 0) dma_v(buf ? vA : vB, Jn);
+    const char *vl = buf ? vB : vA;
+    // many sources: chunk by chunk, four sources at a time
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        // (unconditional: a missing next block has zero-length descriptors, so
-        // the wait counts stay static)
-        if (kc + 1 < KC)
-          load4(ta[(kc + 1) & 1], Sc, kc + 1);
-        else
-          load4(ta[KC & 1], Sn, 0);
-        // keep the prefetch ahead of this chunk's work (the scheduler would
-        // otherwise sink it next to its first use)
-        __builtin_amdgcn_sched_barrier(0);
-        float mix[8];
+    for (int kc = 0; kc < KC; ++kc) {
+      float mix[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) mix[e] = 0.f;
+      for (int e = 0; e < 8; ++e) mix[e] = 0.f;
+      for (int q0 = 0; q0 < ns; q0 += 4) {
+        u32x4 va[4];
+        uint32_t cl[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) mix_src(mix, ta[kc & 1][u], Sc.c[u]);
-        finish_chunk(mix, vl, kc);
-      }
-      if constexpr (KC & 1) {
-        // odd chunk count: the next block's first chunk went to buffer 1
-#pragma unroll
-        for (int u = 0; u < 4; ++u) ta[0][u] = ta[1][u];
-      }
-      Sc = Sn;
-    };
-    // two blocks per trip so each one's V buffers are fixed arrays
-    while (J >= 0) {
-      int Jn = next_J(J + 1);
-      block(J, Jn, vA, vB);
-      J = Jn;
-      if (J < 0) break;
-      Jn = next_J(J + 1);
-      block(J, Jn, vB, vA);
-      J = Jn;
-    }
-  } else {
-    int buf = 0;
-    while (J >= 0) {
-      const int Jn = next_J(J + 1);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (Jn >= 0) dma_v(buf ? vA : vB, Jn);
-      const char *vl = buf ? vB : vA;
-      // many sources: chunk by chunk, four sources at a time
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        float mix[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) mix[e] = 0.f;
-        for (int q0 = 0; q0 < ns; q0 += 4) {
-          u32x4 va[4];
-          uint32_t cl[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            cl[u] = 0u;
-            const int q = q0 + u;
-            if (q >= ns) continue;
-            const int64_t ti = tile_of(q, J);
-            if (ti < 0) continue;
-            va[u] = *reinterpret_cast<const u32x4 *>(rowbase + ti * (int64_t)(B * B) + kc * 512);
-            cl[u] = (uint32_t)coef[q * B + r0];
-          }
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            if (cl[u] != 0u) mix_src(mix, va[u], cl[u]);
+        for (int u = 0; u < 4; ++u) {
+          cl[u] = 0u;
+          const int q = q0 + u;
+          if (q >= ns) continue;
+          const int64_t ti = tile_of(q, J);
+          if (ti < 0) continue;
+          va[u] = *reinterpret_cast<const u32x4 *>(rowbase + ti * (int64_t)(B * B) + kc * 512);
+          cl[u] = (uint32_t)coef[q * B + r0];
         }
-        finish_chunk(mix, vl, kc);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (cl[u] != 0u) mix_src(mix, va[u], cl[u]);
       }
-      buf ^= 1;
-      J = Jn;
+      finish_chunk(mix, vl, kc);
     }
+    buf ^= 1;
+    J = Jn;
   }
 
   float *ot = o + (int64_t)t * T * D;
@@ -413,37 +651,43 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(4))) void
   }
 }
 
-
-
 template <int B, int D>
 static mf_status launch_apply(hipStream_t s, const mf_bsr_map *map, const float *W, int32_t Ht,
                               const void *v, int32_t Hkv, const SeqGeom &g, int32_t renorm,
                               float *o, void *ws, const VtWs &w) {
   const int nbw = (g.maxnb + 31) / 32 > 0 ? (g.maxnb + 31) / 32 : 1;
-  const size_t smem = apply_smem(B, D, map->num_heads, nbw);
-  if (smem > 160 * 1024) return MF_ERR_UNSUPPORTED;
+  const size_t smem = apply_smem(B, map->num_heads, nbw);
+  // tile indices are held in int32; V rows are addressed with 32-bit byte
+  // offsets d * NBR * B * 2
+  if (map->capacity_tiles > INT32_MAX) return MF_ERR_UNSUPPORTED;
+  if ((int64_t)D * g.NBR * B * 2 >= ((int64_t)1 << 31)) return MF_ERR_UNSUPPORTED;
+  const size_t vbufs = 2 * (size_t)B * D * 2;  // the two static V tile buffers
+  if (smem + vbufs > 160 * 1024) return MF_ERR_UNSUPPORTED;
   hipLaunchKernelGGL((k_vtranspose<B, D>), dim3(g.NBR, Hkv), dim3(256), 0, s,
                      reinterpret_cast<const uint16_t *>(v), g.T, at<RowInfo>(ws, w.rt.rows), g.NBR,
                      at<uint16_t>(ws, w.vt));
   if (hip_status() != MF_OK) return MF_ERR_HIP;
-  if (smem > 64 * 1024) {
-    hipFuncSetAttribute(reinterpret_cast<const void *>(&k_apply<B, D, false>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    hipFuncSetAttribute(reinterpret_cast<const void *>(&k_apply<B, D, true>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  if (smem + vbufs > 64 * 1024) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&k_apply4<B, D>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess ||
+        hipFuncSetAttribute(reinterpret_cast<const void *>(&k_apply_many<B, D>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
+      return MF_ERR_HIP;
   }
   const int64_t npos = ((int64_t)g.NBR + kXcds - 1) / kXcds * kXcds;
   // one launch per source-count class; a work-group whose target is of the other
   // class returns right after reading its weight row
-  hipLaunchKernelGGL((k_apply<B, D, false>), dim3((unsigned)(npos * Ht)), dim3(B * 4), smem, s,
-                     map->row_ptr, map->col_idx, map->tiles, map->kept_mass, map->num_heads,
-                     g.NBR, g.T, W, Ht, Ht / Hkv, at<uint16_t>(ws, w.vt),
-                     at<RowInfo>(ws, w.rt.rows), at<int32_t>(ws, w.rt.sched), nbw, map->capacity_tiles, renorm, o);
+  hipLaunchKernelGGL((k_apply4<B, D>), dim3((unsigned)(npos * Ht)), dim3(Apply4Cfg<B, D>::NT),
+                     smem, s, map->row_ptr, map->col_idx, map->tiles, map->kept_mass,
+                     map->num_heads, g.NBR, g.T, W, Ht, Ht / Hkv, at<uint16_t>(ws, w.vt),
+                     at<RowInfo>(ws, w.rt.rows), at<int32_t>(ws, w.rt.sched), nbw,
+                     map->capacity_tiles, renorm, o);
   if (hip_status() != MF_OK) return MF_ERR_HIP;
-  hipLaunchKernelGGL((k_apply<B, D, true>), dim3((unsigned)(npos * Ht)), dim3(B * 4), smem, s,
-                     map->row_ptr, map->col_idx, map->tiles, map->kept_mass, map->num_heads,
-                     g.NBR, g.T, W, Ht, Ht / Hkv, at<uint16_t>(ws, w.vt),
-                     at<RowInfo>(ws, w.rt.rows), at<int32_t>(ws, w.rt.sched), nbw, map->capacity_tiles, renorm, o);
+  hipLaunchKernelGGL((k_apply_many<B, D>), dim3((unsigned)(npos * Ht)),
+                     dim3(ApplyManyCfg<B, D>::NT), smem, s, map->row_ptr, map->col_idx,
+                     map->tiles, map->kept_mass, map->num_heads, g.NBR, g.T, W, Ht, Ht / Hkv,
+                     at<uint16_t>(ws, w.vt), at<RowInfo>(ws, w.rt.rows),
+                     at<int32_t>(ws, w.rt.sched), nbw, map->capacity_tiles, renorm, o);
   return hip_status();
 }
 
