@@ -33,6 +33,9 @@ def hipcc() -> str:
 def flags(extra=()):
     return ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # no NaN ever reaches the kernels: fmax/fmin then need no operand
+            # canonicalisation (infinities are still honoured; -inf marks masked logits)
+            "-fno-honor-nans", "-mno-amdgpu-ieee",
             "-Wno-unused-command-line-argument", "-I" + os.path.join(ROOT, "include"), *extra]
 
 

@@ -82,6 +82,18 @@ __device__ __forceinline__ float half_sum(float v) {
 
 __device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
 
+// Lanes l and l ^ 32 combined with one VALU swap (no LDS): v_permlane32_swap
+// of v with itself gives every lane v[l % 32] in the first result and
+// v[l % 32 + 32] in the second, so both halves get bitwise the same value.
+__device__ __forceinline__ float pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // ---------------------------------------------------------------------------
 // Block-row table, built once per call from the device sequence offsets.
 // Global block-row gr -> (sequence, block index in the sequence), and a

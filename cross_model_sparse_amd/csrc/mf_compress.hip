@@ -36,7 +36,7 @@ struct SelectCfg {
   static constexpr int OFF_BM = OFF_TSUM + (C::NT + 1) * 8;  // tsum[NT + 1]
   static constexpr int OFF_KC = OFF_BM + 32 * 4;             // bm[32]
   static constexpr int EPI = OFF_KC + 16;
-  static constexpr int SMEM = C::KBYTES > EPI ? C::KBYTES : EPI;
+  static constexpr int SMEM = 2 * C::KBYTES > EPI ? 2 * C::KBYTES : EPI;  // two K tiles
 };
 
 template <int B, int D, bool F32>
@@ -68,6 +68,8 @@ __global__ __launch_bounds__(B * 2) __attribute__((amdgpu_waves_per_eu(F32 ? 1 :
   QOp<D, F32> qo;
   load_q<D>(qo, rvalid ? qh + (tok0 + i_pos) * D : nullptr, hl);
 
+  // K tiles alternate between two LDS buffers: block J is read from buffer
+  // J & 1 while block J + 1 is written to the other one, one barrier per block.
   u32x4 stg[C::NCH];
   gload_tile<B, D, F32>(stg, kh, tok0, min(B, L), tid);
   lstore_tile<B, D, F32>(smem, stg, tid);
@@ -75,21 +77,31 @@ __global__ __launch_bounds__(B * 2) __attribute__((amdgpu_waves_per_eu(F32 ? 1 :
 
   float m_run = -INFINITY;
   for (int J = 0; J <= I; ++J) {
+    const char *kcur = smem + (J & 1) * C::KBYTES;
+    char *knext = smem + ((J + 1) & 1) * C::KBYTES;
     if (J < I) gload_tile<B, D, F32>(stg, kh, tok0 + (int64_t)(J + 1) * B, min(B, L - (J + 1) * B), tid);
     f32x16 acc[B / 32];
-    st_tile<B, D>(acc, smem, qo, lane);
-    const bool plain = plain_tile(I, J, B, bias.sink_n, bias.sink2, bias.local_w, bias.local2);
-    float mx = logits_inplace<B>(acc, plain, rvalid, i_pos, J * B, scale2, bias.sink_n,
-                                 bias.sink2, bias.local_w, bias.local2, lane);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    float sum = 0.f;
-    if (mx != -INFINITY) sum = lane_expsum<B>(acc, mx);
-    sum += __shfl_xor(sum, 32, kWave);
-    const float lse = (mx == -INFINITY) ? -INFINITY : mx + fast_log2(sum);
+    st_tile<B, D>(acc, kcur, qo, lane);
+    float lse, off;
+    if (uniform_tile(I, J, B, bias.sink_n, bias.sink2, bias.local_w, bias.local2, off)) {
+      // the scale is positive: the largest scaled logit is the image of the
+      // largest raw score, and the offset cancels inside the sum
+      const float mr = pair_max(lane_rawmax<B>(acc));
+      const float sum = pair_sum(lane_expsum_fma<B>(acc, scale2, -mr * scale2));
+      lse = rvalid ? fmaf(mr, scale2, off) + fast_log2(sum) : -INFINITY;
+    } else {
+      float mx = logits_inplace<B>(acc, false, rvalid, i_pos, J * B, scale2, bias.sink_n,
+                                   bias.sink2, bias.local_w, bias.local2, lane);
+      mx = pair_max(mx);
+      float sum = 0.f;
+      if (mx != -INFINITY) sum = lane_expsum<B>(acc, mx);
+      sum = pair_sum(sum);
+      lse = (mx == -INFINITY) ? -INFINITY : mx + fast_log2(sum);
+    }
     if (hl == 0) part[(int64_t)J * B + i_loc] = lse;
     m_run = fmaxf(m_run, lse);
-    __syncthreads();
-    if (J < I) lstore_tile<B, D, F32>(smem, stg, tid);
+    // the other buffer held block J - 1, whose readers all passed the last barrier
+    if (J < I) lstore_tile<B, D, F32>(knext, stg, tid);
     __syncthreads();
   }
 
@@ -240,12 +252,41 @@ __global__ __launch_bounds__(1024) void k_offsets(const int32_t *__restrict__ co
 template <int B, int D, bool F32>
 struct TilesCfg {
   using C = QKCfg<B, D, F32>;
-  static constexpr int TPITCH = B * 2 + kLdsPad;   // bf16 tile row pitch in LDS
-  static constexpr int TBYTES = B * TPITCH;
   static constexpr int LIST = kMaxNB * 4 + 64 * 4;
-  static constexpr int SMEM = C::KBYTES + TBYTES + LIST;
-  static constexpr int TCH = B * B * 2 / 16 / C::NT;  // 16-byte tile chunks per thread
+  static constexpr int SMEM = 2 * C::KBYTES + LIST;   // two K tiles + kept list
 };
+
+// Probabilities of one lane's 4 consecutive keys (fp32) -> two bf16 pairs, RNE.
+__device__ __forceinline__ uint2 pack4(float p0, float p1, float p2, float p3) {
+  uint2 w;
+  w.x = pack_bf16x2(p0, p1);
+  w.y = pack_bf16x2(p2, p3);
+  return w;
+}
+
+// One wave's 32 rows of a kept tile, from the S^T accumulators to the map in
+// fragment order.  Lane (m, hl) holds row m and, per 32-key group and 8-key
+// run q, keys 8q + 4hl .. + 3.  One v_permlane32_swap per word pair hands lanes
+// 0-31 the full 8-key run q = 2p and lanes 32-63 the run q = 2p + 1, which is
+// one 16-byte chunk of the fragment-ordered tile: row group i / 16, key chunk
+// mb, position (q * 16 + i % 16).
+template <int B>
+__device__ __forceinline__ void store_tile_rows(char *dst, const uint2 (&w)[B / 32][4], int wave,
+                                                int lane) {
+  const int m = lane & 31, hl = lane >> 5;
+  const int i_loc = wave * 32 + m;
+#pragma unroll
+  for (int mb = 0; mb < B / 32; ++mb)
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr) {
+      const auto s0 = __builtin_amdgcn_permlane32_swap(w[mb][2 * pr].x, w[mb][2 * pr + 1].x, false, false);
+      const auto s1 = __builtin_amdgcn_permlane32_swap(w[mb][2 * pr].y, w[mb][2 * pr + 1].y, false, false);
+      const u32x4 chunk = u32x4{s0[0], s1[0], s0[1], s1[1]};
+      const int q = 2 * pr + hl;
+      const int off = (((i_loc >> 4) * (B / 32) + mb) * 64 + q * 16 + (i_loc & 15)) * 16;
+      *reinterpret_cast<u32x4 *>(dst + off) = chunk;
+    }
+}
 
 template <int B, int D, bool F32>
 __global__ __launch_bounds__(B * 2) __attribute__((amdgpu_waves_per_eu(F32 ? 1 : 2))) void k_tiles(
@@ -258,9 +299,7 @@ __global__ __launch_bounds__(B * 2) __attribute__((amdgpu_waves_per_eu(F32 ? 1 :
   using TC = TilesCfg<B, D, F32>;
   using E = std::conditional_t<F32, float, uint16_t>;
   __shared__ __attribute__((aligned(16))) char smem[TC::SMEM];
-  char *klds = smem;
-  char *tlds = smem + C::KBYTES;
-  int32_t *list = reinterpret_cast<int32_t *>(smem + C::KBYTES + TC::TBYTES);
+  int32_t *list = reinterpret_cast<int32_t *>(smem + 2 * C::KBYTES);
   int32_t *woff = list + kMaxNB;  // [33] word offsets
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -307,56 +346,54 @@ __global__ __launch_bounds__(B * 2) __attribute__((amdgpu_waves_per_eu(F32 ? 1 :
   const char *kh = reinterpret_cast<const char *>(kv) + (int64_t)h * T * D * C::ESZ;
   QOp<D, F32> qo;
   load_q<D>(qo, rvalid ? qh + (tok0 + i_pos) * D : nullptr, hl);
-  const float lse2 = rvalid ? lse2_in[(int64_t)h * T + tok0 + i_pos] : 0.f;
+  // rows past the sequence end: -lse = -inf makes every probability exactly 0
+  const float nlse2 = rvalid ? -lse2_in[(int64_t)h * T + tok0 + i_pos] : -INFINITY;
 
+  // K tiles alternate between two LDS buffers: tile c is read from buffer c & 1
+  // while tile c + 1 is written to the other one, one barrier per tile.
   u32x4 stg[C::NCH];
   {
     const int J = list[0];
     gload_tile<B, D, F32>(stg, kh, tok0 + (int64_t)J * B, min(B, L - J * B), tid);
-    lstore_tile<B, D, F32>(klds, stg, tid);
+    lstore_tile<B, D, F32>(smem, stg, tid);
   }
   __syncthreads();
   for (int c = 0; c < cnt; ++c) {
     const int J = list[c];
+    const char *kcur = smem + (c & 1) * C::KBYTES;
+    char *knext = smem + ((c + 1) & 1) * C::KBYTES;
     if (c + 1 < cnt) {
       const int Jn = list[c + 1];
       gload_tile<B, D, F32>(stg, kh, tok0 + (int64_t)Jn * B, min(B, L - Jn * B), tid);
     }
     f32x16 acc[B / 32];
-    st_tile<B, D>(acc, klds, qo, lane);
-    const bool plain = plain_tile(I, J, B, bias.sink_n, bias.sink2, bias.local_w, bias.local2);
-    logits_inplace<B>(acc, plain, rvalid, i_pos, J * B, scale2, bias.sink_n, bias.sink2,
-                      bias.local_w, bias.local2, lane);
-    // probabilities -> bf16, written transposed into the LDS tile [i][j]
+    st_tile<B, D>(acc, kcur, qo, lane);
+    uint2 w[B / 32][4];
+    float off;
+    if (uniform_tile(I, J, B, bias.sink_n, bias.sink2, bias.local_w, bias.local2, off)) {
+      const float c0 = nlse2 + off;
 #pragma unroll
-    for (int mb = 0; mb < B / 32; ++mb)
+      for (int mb = 0; mb < B / 32; ++mb)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float pv[4];
+        for (int g = 0; g < 4; ++g)
+          w[mb][g] = pack4(fast_exp2(fmaf(acc[mb][4 * g + 0], scale2, c0)),
+                           fast_exp2(fmaf(acc[mb][4 * g + 1], scale2, c0)),
+                           fast_exp2(fmaf(acc[mb][4 * g + 2], scale2, c0)),
+                           fast_exp2(fmaf(acc[mb][4 * g + 3], scale2, c0)));
+    } else {
+      logits_inplace<B>(acc, false, rvalid, i_pos, J * B, scale2, bias.sink_n, bias.sink2,
+                        bias.local_w, bias.local2, lane);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pv[e] = rvalid ? fast_exp2(acc[mb][4 * g + e] - lse2) : 0.f;
-        uint2 w;
-        w.x = pack_bf16x2(pv[0], pv[1]);
-        w.y = pack_bf16x2(pv[2], pv[3]);
-        const int j_loc = mb * 32 + 8 * g + 4 * hl;
-        *reinterpret_cast<uint2 *>(tlds + i_loc * TC::TPITCH + j_loc * 2) = w;
-      }
-    __syncthreads();
-    if (c + 1 < cnt) lstore_tile<B, D, F32>(klds, stg, tid);
-    if (base + c < capacity) {
-      char *dst = reinterpret_cast<char *>(tiles + (base + c) * (int64_t)B * B);
+      for (int mb = 0; mb < B / 32; ++mb)
 #pragma unroll
-      for (int k = 0; k < TC::TCH; ++k) {
-        // fragment order: 16-byte chunk q = (row group * KC + key chunk) * 64 + f
-        // holds row 16 * group + f % 16, keys 32 * chunk + 8 * (f / 16) .. + 8
-        const int q = tid + k * C::NT;
-        const int blk = q >> 6, f = q & 63;
-        const int rr = (blk / (B / 32)) * 16 + (f & 15);
-        const int c0 = (blk % (B / 32)) * 32 + 8 * (f >> 4);
-        *reinterpret_cast<u32x4 *>(dst + q * 16) =
-            *reinterpret_cast<const u32x4 *>(tlds + rr * TC::TPITCH + c0 * 2);
-      }
+        for (int g = 0; g < 4; ++g)
+          w[mb][g] = pack4(fast_exp2(acc[mb][4 * g + 0] + nlse2), fast_exp2(acc[mb][4 * g + 1] + nlse2),
+                           fast_exp2(acc[mb][4 * g + 2] + nlse2), fast_exp2(acc[mb][4 * g + 3] + nlse2));
     }
+    if (base + c < capacity)
+      store_tile_rows<B>(reinterpret_cast<char *>(tiles + (base + c) * (int64_t)B * B), w, wave, lane);
+    // the other buffer held tile c - 1, whose readers all passed the last barrier
+    if (c + 1 < cnt) lstore_tile<B, D, F32>(knext, stg, tid);
     __syncthreads();
   }
 }

@@ -170,12 +170,62 @@ __device__ __forceinline__ float logits_inplace(f32x16 (&acc)[B / 32], bool plai
 }
 
 // Tile class of key block J for query block I (uniform over a work-group).
+// `plain`: strictly below the diagonal, no sink column, no local-window element.
 __device__ __forceinline__ bool plain_tile(int I, int J, int B, int sink_n, float sink2,
                                            int local_w, float local2) {
   if (J >= I) return false;
   if (sink2 != 0.f && J * B < sink_n) return false;
   if (local2 != 0.f && I * B - (J * B + B - 1) < local_w) return false;
   return true;
+}
+
+// `uniform`: strictly below the diagonal, no sink column, and the local window
+// covers either all of the tile or none of it, so every element gets the same
+// offset `off` (log2 units).  Rows i of block I and keys j of block J < I differ
+// by (I - J) * B - (B - 1) .. (I - J) * B + (B - 1).
+__device__ __forceinline__ bool uniform_tile(int I, int J, int B, int sink_n, float sink2,
+                                             int local_w, float local2, float &off) {
+  off = 0.f;
+  if (J >= I) return false;
+  if (sink2 != 0.f && J * B < sink_n) return false;
+  if (local2 != 0.f) {
+    const int dmin = (I - J) * B - (B - 1), dmax = (I - J) * B + (B - 1);
+    if (dmax < local_w)
+      off = local2;
+    else if (dmin < local_w)
+      return false;
+  }
+  return true;
+}
+
+// Lane maximum of the raw scores (before scaling), three at a time.
+template <int B>
+__device__ __forceinline__ float lane_rawmax(const f32x16 (&acc)[B / 32]) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int mb = 0; mb < B / 32; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) mx = max3(mx, acc[mb][r], acc[mb][r + 1]);
+  return mx;
+}
+
+// Sum of exp2(acc * scale2 + c) over the lane's values, pairwise within each
+// 16-group.
+template <int B>
+__device__ __forceinline__ float lane_expsum_fma(const f32x16 (&acc)[B / 32], float scale2, float c) {
+  float tot = 0.f;
+#pragma unroll
+  for (int mb = 0; mb < B / 32; ++mb) {
+    float e[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) e[r] = fast_exp2(fmaf(acc[mb][r], scale2, c));
+#pragma unroll
+    for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+      for (int r = 0; r < w; ++r) e[r] += e[r + w];
+    tot += e[0];
+  }
+  return tot;
 }
 
 // Sum of exp2(x - mx) over the lane's values, pairwise within each 16-group.
