@@ -82,6 +82,11 @@ __device__ __forceinline__ float half_sum(float v) {
 
 __device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
 
+// Index of the calling wave in its work-group, as a value the compiler knows to
+// be wave-uniform (held in a scalar register): buffer descriptors and scalar
+// offsets built from it then need no per-lane waterfall loop.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 // Lanes l and l ^ 32 combined with one VALU swap (no LDS): v_permlane32_swap
 // of v with itself gives every lane v[l % 32] in the first result and
 // v[l % 32 + 32] in the second, so both halves get bitwise the same value.

@@ -50,7 +50,7 @@ __global__ __launch_bounds__(B * 2) __attribute__((amdgpu_waves_per_eu(F32 ? 1 :
   using E = std::conditional_t<F32, float, uint16_t>;
   __shared__ __attribute__((aligned(16))) char smem[SelectCfg<B, D, F32>::SMEM];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int m = lane & 31, hl = lane >> 5;
   const int pos = blockIdx.x / Hs, h = blockIdx.x % Hs;
   const int gr = sched[pos];
@@ -302,7 +302,7 @@ __global__ __launch_bounds__(B * 2) __attribute__((amdgpu_waves_per_eu(F32 ? 1 :
   int32_t *list = reinterpret_cast<int32_t *>(smem + 2 * C::KBYTES);
   int32_t *woff = list + kMaxNB;  // [33] word offsets
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int m = lane & 31, hl = lane >> 5;
   const int pos = blockIdx.x / Hs, h = blockIdx.x % Hs;
   const int gr = sched[pos];

@@ -46,7 +46,7 @@ __global__ __launch_bounds__(kDenseB * 2) void k_dense(
   char *klds = smem;
   char *vlds = smem + C::KBYTES;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int m = lane & 31, hl = lane >> 5;
   const int pos = blockIdx.x / Hq, h = blockIdx.x % Hq;
   const int g = h / grp;
