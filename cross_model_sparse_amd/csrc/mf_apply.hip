@@ -352,7 +352,7 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(4))) void
     int32_t NBR, int64_t T, const float *__restrict__ W, int32_t Ht, int32_t grp,
     const uint16_t *__restrict__ vt, const RowInfo *__restrict__ rows,
     const int32_t *__restrict__ sched, int32_t nbw, int64_t capacity, int32_t renorm,
-    float *__restrict__ o) {
+    float *__restrict__ o, const int32_t *__restrict__ row_alias) {
   using C = Apply4Cfg<B, D>;
   constexpr int KC = C::KC, NR = C::NR, TB = C::TB, DQ = C::DQ;
   // separate arrays, so the compiler can tell that direct loads into one never
@@ -375,9 +375,13 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(4))) void
   const int64_t tok0 = (int64_t)ri.start;
   const int64_t tpad = (int64_t)NBR * B;
 
-  const int ns = row_sources<C::NT>(mp, W, t, Hs, row_ptr, NBR, gr, tid);
+  // BSR row of this block-row: its own, or that of the earlier block-row it
+  // shares (tiles and kept masses are equal; V and O stay this row's own)
+  const int ga = row_alias ? row_alias[gr] : gr;
+  const int grm = (ga >= 0 && ga < NBR) ? ga : gr;
+  const int ns = row_sources<C::NT>(mp, W, t, Hs, row_ptr, NBR, grm, tid);
   if (ns > 4) return;  // handled by k_apply_many
-  row_maps_fill<B, C::NT>(mp, ns, row_ptr, col_idx, capacity, kept_mass, T, NBR, gr, tok0, I, L,
+  row_maps_fill<B, C::NT>(mp, ns, row_ptr, col_idx, capacity, kept_mass, T, NBR, grm, tok0, I, L,
                           (n + 31) / 32, renorm, tid);
 
   // coefficients of this lane's two rows, [c, 0] and [0, c] bf16 pairs (zero
@@ -542,7 +546,7 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(4))) void
     int32_t NBR, int64_t T, const float *__restrict__ W, int32_t Ht, int32_t grp,
     const uint16_t *__restrict__ vt, const RowInfo *__restrict__ rows,
     const int32_t *__restrict__ sched, int32_t nbw, int64_t capacity, int32_t renorm,
-    float *__restrict__ o) {
+    float *__restrict__ o, const int32_t *__restrict__ row_alias) {
   using C = ApplyManyCfg<B, D>;
   constexpr int KC = C::KC;
   __shared__ __attribute__((aligned(16))) char vA[C::VBYTES];
@@ -563,9 +567,13 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(4))) void
   const int64_t tok0 = (int64_t)ri.start;
   const int64_t tpad = (int64_t)NBR * B;
 
-  const int ns = row_sources<C::NT>(mp, W, t, Hs, row_ptr, NBR, gr, tid);
+  // BSR row of this block-row: its own, or that of the earlier block-row it
+  // shares (tiles and kept masses are equal; V and O stay this row's own)
+  const int ga = row_alias ? row_alias[gr] : gr;
+  const int grm = (ga >= 0 && ga < NBR) ? ga : gr;
+  const int ns = row_sources<C::NT>(mp, W, t, Hs, row_ptr, NBR, grm, tid);
   if (ns <= 4) return;  // handled by k_apply4
-  row_maps_fill<B, C::NT>(mp, ns, row_ptr, col_idx, capacity, kept_mass, T, NBR, gr, tok0, I, L,
+  row_maps_fill<B, C::NT>(mp, ns, row_ptr, col_idx, capacity, kept_mass, T, NBR, grm, tok0, I, L,
                           (n + 31) / 32, renorm, tid);
   auto next_J = [&](int from) -> int { return union_next(mp, n, from); };
   auto tile_of = [&](int q, int J) -> int64_t { return tile_index(mp, q, J, capacity); };
@@ -681,13 +689,15 @@ static mf_status launch_apply(hipStream_t s, const mf_bsr_map *map, const float 
                      smem, s, map->row_ptr, map->col_idx, map->tiles, map->kept_mass,
                      map->num_heads, g.NBR, g.T, W, Ht, Ht / Hkv, at<uint16_t>(ws, w.vt),
                      at<RowInfo>(ws, w.rt.rows), at<int32_t>(ws, w.rt.sched), nbw,
-                     map->capacity_tiles, renorm, o);
+                     map->capacity_tiles, renorm, o,
+                     map->row_alias);
   if (hip_status() != MF_OK) return MF_ERR_HIP;
   hipLaunchKernelGGL((k_apply_many<B, D>), dim3((unsigned)(npos * Ht)),
                      dim3(ApplyManyCfg<B, D>::NT), smem, s, map->row_ptr, map->col_idx,
                      map->tiles, map->kept_mass, map->num_heads, g.NBR, g.T, W, Ht, Ht / Hkv,
                      at<uint16_t>(ws, w.vt), at<RowInfo>(ws, w.rt.rows),
-                     at<int32_t>(ws, w.rt.sched), nbw, map->capacity_tiles, renorm, o);
+                     at<int32_t>(ws, w.rt.sched), nbw, map->capacity_tiles, renorm, o,
+                     map->row_alias);
   return hip_status();
 }
 

@@ -45,7 +45,8 @@ __global__ __launch_bounds__(B * 2) __attribute__((amdgpu_waves_per_eu(F32 ? 1 :
     const RowInfo *__restrict__ rows, const int32_t *__restrict__ sched,
     const int64_t *__restrict__ pbase, int64_t ptot, float scale2, BiasArgs bias, double p,
     float *__restrict__ lse2_out, float *__restrict__ partials, int32_t *__restrict__ counts,
-    uint32_t *__restrict__ bitmaps, int32_t nbw, float *__restrict__ kept_mass) {
+    uint32_t *__restrict__ bitmaps, int32_t nbw, float *__restrict__ kept_mass,
+    const int32_t *__restrict__ row_alias) {
   using C = QKCfg<B, D, F32>;
   using E = std::conditional_t<F32, float, uint16_t>;
   __shared__ __attribute__((aligned(16))) char smem[SelectCfg<B, D, F32>::SMEM];
@@ -54,6 +55,14 @@ __global__ __launch_bounds__(B * 2) __attribute__((amdgpu_waves_per_eu(F32 ? 1 :
   const int m = lane & 31, hl = lane >> 5;
   const int pos = blockIdx.x / Hs, h = blockIdx.x % Hs;
   const int gr = sched[pos];
+  if (row_alias && row_alias[gr] != gr && row_alias[gr] >= 0 && row_alias[gr] < NBR) {
+    // shares an earlier block-row: no tiles of its own (kept mass is copied
+    // once the first copy is done)
+    const int64_t r = (int64_t)h * NBR + gr;
+    for (int w = tid; w < nbw; w += C::NT) bitmaps[r * nbw + w] = 0u;
+    if (tid == 0) counts[r] = 0;
+    return;
+  }
   const RowInfo ri = rows[gr];
   const int I = ri.blk, L = ri.len;
   const int i_loc = wave * 32 + m;
@@ -209,6 +218,27 @@ __global__ __launch_bounds__(B * 2) __attribute__((amdgpu_waves_per_eu(F32 ? 1 :
   if (rvalid && hl == 0) {
     kept_mass[(int64_t)h * T + tok0 + i_pos] = (float)ks;
     lse2_out[(int64_t)h * T + tok0 + i_pos] = lse2;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// k_alias_kmass: block-rows that share an earlier one take its kept masses
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_alias_kmass(const RowInfo *__restrict__ rows,
+                                                     const int32_t *__restrict__ row_alias,
+                                                     int32_t NBR, int32_t Hs, int64_t T, int32_t B,
+                                                     float *__restrict__ kept_mass) {
+  const int gr = blockIdx.x;
+  const int src = row_alias[gr];
+  if (src == gr || src < 0 || src >= NBR) return;
+  const RowInfo a = rows[gr], b = rows[src];
+  // rows valid in both block-rows (all B for the full block-rows sharing is set on)
+  const int nv = min(B, min(a.len - a.blk * B, b.len - b.blk * B));
+  const int64_t t_dst = (int64_t)a.start + (int64_t)a.blk * B;
+  const int64_t t_src = (int64_t)b.start + (int64_t)b.blk * B;
+  for (int idx = threadIdx.x; idx < Hs * nv; idx += blockDim.x) {
+    const int h = idx / nv, i = idx % nv;
+    kept_mass[(int64_t)h * T + t_dst + i] = kept_mass[(int64_t)h * T + t_src + i];
   }
 }
 
@@ -412,8 +442,13 @@ static mf_status launch_compress(hipStream_t s, const void *q, const void *k, co
                      at<RowInfo>(ws, w.rt.rows), at<int32_t>(ws, w.rt.sched),
                      at<int64_t>(ws, w.rt.pbase), ptot, scale2, ba, p, at<float>(ws, w.lse2),
                      at<float>(ws, w.partials), at<int32_t>(ws, w.counts),
-                     at<uint32_t>(ws, w.bitmaps), w.nbw, map->kept_mass);
+                     at<uint32_t>(ws, w.bitmaps), w.nbw, map->kept_mass, map->row_alias);
   if (hip_status() != MF_OK) return MF_ERR_HIP;
+  if (map->row_alias) {
+    hipLaunchKernelGGL(k_alias_kmass, dim3(g.NBR), dim3(256), 0, s, at<RowInfo>(ws, w.rt.rows),
+                       map->row_alias, g.NBR, Hs, g.T, B, map->kept_mass);
+    if (hip_status() != MF_OK) return MF_ERR_HIP;
+  }
   hipLaunchKernelGGL(k_offsets, dim3(1), dim3(1024), 0, s, at<int32_t>(ws, w.counts),
                      (int64_t)Hs * g.NBR, map->capacity_tiles, map->row_ptr, map->nnz,
                      map->status);

@@ -23,7 +23,7 @@ MF_BF16, MF_FP32 = 0, 1
 EXPORTS = ("mf_num_block_rows", "mf_compress_max_tiles", "mf_compress_workspace_bytes",
            "mf_compress_topp", "mf_apply_workspace_bytes", "mf_apply_translated",
            "mf_dense_workspace_bytes", "mf_dense_ref_attention", "mf_read_status",
-           "mf_status_string")
+           "mf_status_string", "mf_prefix_dedupe_workspace_bytes", "mf_prefix_dedupe")
 
 
 class MfLogitBias(ctypes.Structure):
@@ -37,7 +37,7 @@ class MfBsrMap(ctypes.Structure):
                 ("capacity_tiles", ctypes.c_int64), ("row_ptr", ctypes.c_void_p),
                 ("col_idx", ctypes.c_void_p), ("tiles", ctypes.c_void_p),
                 ("kept_mass", ctypes.c_void_p), ("nnz", ctypes.c_void_p),
-                ("status", ctypes.c_void_p)]
+                ("status", ctypes.c_void_p), ("row_alias", ctypes.c_void_p)]
 
 
 class MapflowError(RuntimeError):
@@ -73,6 +73,8 @@ def load():
                                          ctypes.POINTER(MfLogitBias), vp, vp, sz]),
         "mf_read_status": (i32, [vp, ctypes.POINTER(MfBsrMap), ctypes.POINTER(i64)]),
         "mf_status_string": (ctypes.c_char_p, [i32]),
+        "mf_prefix_dedupe_workspace_bytes": (sz, [pcu, i32, i32]),
+        "mf_prefix_dedupe": (i32, [vp, vp, vp, i32, pcu, vp, i32, i32, i32, i32, vp, vp, sz]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -166,6 +168,7 @@ class BsrMap:
     kept_mass: torch.Tensor    # float32 [Hs, T]
     nnz: torch.Tensor          # int64 [1]
     status: torch.Tensor       # int32 [1]
+    row_alias: Optional[torch.Tensor] = None  # int32 [NBR] from mf_prefix_dedupe, or None
 
     @property
     def capacity(self) -> int:
@@ -175,7 +178,8 @@ class BsrMap:
         return MfBsrMap(self.num_heads, self.block, self.num_block_rows, self.total_tokens,
                         self.capacity, self.row_ptr.data_ptr(), self.col_idx.data_ptr(),
                         self.tiles.data_ptr(), self.kept_mass.data_ptr(), self.nnz.data_ptr(),
-                        self.status.data_ptr())
+                        self.status.data_ptr(),
+                        self.row_alias.data_ptr() if self.row_alias is not None else None)
 
 
 def alloc_map(Hs: int, cu_seqlens, B: int, device, capacity: Optional[int] = None) -> BsrMap:
@@ -195,11 +199,46 @@ def alloc_map(Hs: int, cu_seqlens, B: int, device, capacity: Optional[int] = Non
                   torch.zeros(1, dtype=torch.int32, device=device))
 
 
+def mf_prefix_dedupe_workspace_bytes(cu_seqlens, B: int) -> int:
+    cu = _cu_host(cu_seqlens)
+    return load().mf_prefix_dedupe_workspace_bytes(_cu_ptr(cu), len(cu) - 1, B)
+
+
+def mf_prefix_dedupe(q: torch.Tensor, k: torch.Tensor, cu_seqlens, B: int,
+                     out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                     cu_dev: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """int32 [NBR]: for every global block-row, the first block-row with the same
+    q/k prefix (itself when unique); pass it to mf_compress_topp as row_alias."""
+    lib = load()
+    cu = _cu_host(cu_seqlens)
+    Hs, T, d = q.shape
+    if k.shape != q.shape or k.dtype != q.dtype or not (q.is_contiguous() and k.is_contiguous()):
+        raise ValueError("q and k must be contiguous, of the same shape and dtype")
+    dev = q.device
+    nbr = mf_num_block_rows(cu, B)
+    if nbr < 0:
+        raise ValueError("invalid sequence offsets or block size")
+    if out is None:
+        out = torch.empty(max(nbr, 1), dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(mf_prefix_dedupe_workspace_bytes(cu, B), dtype=torch.uint8, device=dev)
+    if cu_dev is None:
+        cu_dev = _dev_cu(cu, dev)
+    st = lib.mf_prefix_dedupe(_stream(), q.data_ptr(), k.data_ptr(), _dtype_code(q), _cu_ptr(cu),
+                              cu_dev.data_ptr(), len(cu) - 1, Hs, d, B, out.data_ptr(),
+                              workspace.data_ptr(), workspace.numel())
+    _check("mf_prefix_dedupe", st)
+    return out[:nbr]
+
+
 def mf_compress_topp(q: torch.Tensor, k: torch.Tensor, cu_seqlens, B: int, p: float,
                      bias: Optional[dict] = None, out: Optional[BsrMap] = None,
                      capacity: Optional[int] = None, workspace: Optional[torch.Tensor] = None,
-                     cu_dev: Optional[torch.Tensor] = None) -> BsrMap:
-    """Block top-p compression of the causal maps of all heads of q, k ([Hs, T, d])."""
+                     cu_dev: Optional[torch.Tensor] = None,
+                     row_alias: Optional[torch.Tensor] = None) -> BsrMap:
+    """Block top-p compression of the causal maps of all heads of q, k ([Hs, T, d]).
+    With row_alias (from mf_prefix_dedupe), block-rows that share an earlier one
+    are not computed; the map keeps the alias for retrieval."""
     lib = load()
     cu = _cu_host(cu_seqlens)
     Hs, T, d = q.shape
@@ -209,6 +248,9 @@ def mf_compress_topp(q: torch.Tensor, k: torch.Tensor, cu_seqlens, B: int, p: fl
         raise ValueError("q and k must be contiguous")
     dev = q.device
     m = out if out is not None else alloc_map(Hs, cu, B, dev, capacity)
+    if row_alias is not None and (row_alias.dtype != torch.int32 or not row_alias.is_contiguous()):
+        raise ValueError("row_alias must be contiguous int32")
+    m.row_alias = row_alias
     if workspace is None:
         workspace = torch.empty(mf_compress_workspace_bytes(Hs, cu, B, d), dtype=torch.uint8, device=dev)
     if cu_dev is None:

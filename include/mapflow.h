@@ -14,6 +14,11 @@
  *                           for every target head, without a dense L x L map in
  *                           device memory.  MapFlow §3.3 (linear head mapping),
  *                           §5.4 (fused retrieval kernel).
+ *   mf_prefix_dedupe        block-rows whose query/key prefix repeats an earlier
+ *                           sequence's, so compression computes them once and
+ *                           both sides read the first copy.  MapFlow §5.3 (Block
+ *                           Manager: blocks indexed by prefix hashes), §2.3
+ *                           (prefix caching).
  *   mf_dense_ref_attention  softmax(Q K^T / sqrt(d) + bias) V, causal, for the
  *                           receiver layers that are recomputed (MapFlow §4) and
  *                           the exact path a cache miss falls back to (AttnCache
@@ -105,7 +110,14 @@ typedef struct mf_logit_bias {
  * The caller allocates every array and sets the pointers and capacity_tiles;
  * mf_compress_topp fills the four size fields and the arrays.  Apply only reads
  * the map, so one map can serve any number of apply calls (MapFlow §5.2: one
- * compressed map serves many receivers). */
+ * compressed map serves many receivers).
+ *
+ * row_alias (optional, NULL for none): [NBR] global block-row -> the block-row
+ * whose rows it shares, as written by mf_prefix_dedupe (itself when unique).
+ * With it, mf_compress_topp computes only block-rows with row_alias[gr] == gr;
+ * the others get no tiles of their own (empty BSR rows) and a copy of their
+ * first copy's kept mass, and mf_apply_translated reads their tiles through the
+ * alias.  Set it before mf_compress_topp and keep it with the map. */
 typedef struct mf_bsr_map {
   int32_t num_heads;       /* Hs                                        (out) */
   int32_t block;           /* B                                         (out) */
@@ -118,6 +130,7 @@ typedef struct mf_bsr_map {
   float *kept_mass;        /* [Hs][T]                                         */
   int64_t *nnz;            /* device scalar: number of kept tiles             */
   int32_t *status;         /* device scalar: MF_OK or MF_ERR_CAPACITY         */
+  const int32_t *row_alias; /* [NBR] or NULL: shared block-rows (see above)     */
 } mf_bsr_map;
 
 /* Number of global block-rows sum_s ceil(L_s / B); -1 if the offsets are invalid.
@@ -156,6 +169,33 @@ mf_status mf_compress_topp(void *stream, const void *q, const void *k, mf_dtype 
                            int32_t nseq, int32_t Hs, int32_t d, int32_t B, double p,
                            const mf_logit_bias *bias, mf_bsr_map *map, void *workspace,
                            size_t workspace_bytes);
+
+/* Device workspace bytes mf_prefix_dedupe needs (0 if the arguments are invalid). */
+size_t mf_prefix_dedupe_workspace_bytes(const int32_t *cu_seqlens_host, int32_t nseq, int32_t B);
+
+/* Shared-prefix block-rows (MapFlow §5.3: the Block Manager indexes compressed
+ * blocks by prefix hashes; §2.3: prefix caching skips recomputation of shared
+ * prefixes).
+ *
+ * Block-row (s, I) is *full* when (I + 1) * B <= L_s.  A full block-row whose
+ * tokens 0 .. (I + 1) B - 1 carry the same q and k values (every head, bit for
+ * bit) as those of an earlier sequence s' < s whose block-row I is also full
+ * has the same causal logits, offsets and probabilities, hence the same kept
+ * blocks, tiles and kept masses.  row_alias[gr] is the global block-row of the
+ * first such (s', I), or gr itself.
+ *
+ * Prefix equality is decided by a 128-bit chained hash of each block's q and k
+ * content (per block: a sum of independently mixed 16-byte chunks; per
+ * sequence: chained from block 0), computed on the device.
+ *
+ * q, k        [Hs][T][d] in qk_dtype, as passed to mf_compress_topp.
+ * row_alias   [NBR] int32, written.
+ * workspace   device, at least mf_prefix_dedupe_workspace_bytes(...) bytes.
+ * Errors: MF_ERR_INVALID_ARG, MF_ERR_UNSUPPORTED, MF_ERR_WORKSPACE, MF_ERR_HIP. */
+mf_status mf_prefix_dedupe(void *stream, const void *q, const void *k, mf_dtype qk_dtype,
+                           const int32_t *cu_seqlens_host, const int32_t *cu_seqlens_dev,
+                           int32_t nseq, int32_t Hs, int32_t d, int32_t B, int32_t *row_alias,
+                           void *workspace, size_t workspace_bytes);
 
 /* Device workspace bytes mf_apply_translated needs: a block-padded, transposed
  * copy of V ([Hkv][d][NBR * B] bf16) plus the block-row table.  0 if invalid. */

@@ -224,6 +224,56 @@ def block_rows(cu: np.ndarray, B: int) -> List[Tuple[int, int]]:
     return out
 
 
+def prefix_alias(q: np.ndarray, k: np.ndarray, cu: np.ndarray, B: int) -> np.ndarray:
+    """Shared block-rows (MapFlow §5.3: compressed blocks indexed by their prefix;
+    §2.3: prefix caching).
+
+    Block-row (s, I) is full when (I + 1) * B <= L_s.  Its compressed rows depend
+    only on q and k of the sequence's tokens 0 .. (I + 1) * B - 1 (causal rows,
+    offsets measured from the sequence start), so a full block-row whose prefix
+    equals, bit for bit over every head, that of an earlier sequence s' whose
+    block-row I is also full shares that block-row.  Returns, per global
+    block-row, the global index of the first such (s', I), or its own index.
+
+    Decided by direct comparison of the arrays (no hashing): for each pair of
+    sequences, the length of their common prefix."""
+    rows = block_rows(cu, B)
+    first = {}
+    g = 0
+    for s, (_, L) in enumerate(seqs(cu)):
+        first[s] = g
+        g += nblocks(L, B)
+    sq = seqs(cu)
+    qb = q.view(np.uint32) if q.dtype == np.float32 else q
+    kb = k.view(np.uint32) if k.dtype == np.float32 else k
+
+    def common(s: int, s2: int) -> int:
+        (a, L), (a2, L2) = sq[s], sq[s2]
+        n = min(L, L2)
+        if n == 0:
+            return 0
+        diff = (np.any(qb[:, a:a + n] != qb[:, a2:a2 + n], axis=(0, 2)) |
+                np.any(kb[:, a:a + n] != kb[:, a2:a2 + n], axis=(0, 2)))
+        idx = np.flatnonzero(diff)
+        return int(idx[0]) if len(idx) else n
+
+    alias = np.arange(len(rows), dtype=np.int32)
+    memo = {}
+    for gr, (s, I) in enumerate(rows):
+        need = (I + 1) * B
+        if need > sq[s][1]:
+            continue
+        for s2 in range(s):
+            if need > sq[s2][1]:
+                continue
+            if (s, s2) not in memo:
+                memo[(s, s2)] = common(s, s2)
+            if memo[(s, s2)] >= need:
+                alias[gr] = first[s2] + I
+                break
+    return alias
+
+
 def compress(q: np.ndarray, k: np.ndarray, cu: np.ndarray, B: int, p: float, bias: dict,
              heads: Optional[Sequence[int]] = None,
              rows: Optional[Sequence[Tuple[int, int]]] = None) -> Dict[Tuple[int, int, int], RowResult]:

@@ -30,7 +30,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = header_functions()
-    assert len(names) == 10
+    assert len(names) == 12
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(mf.EXPORTS) == names
@@ -90,7 +90,7 @@ def test_apply_and_dense_reject_bad_arguments(lib):
     c = cu([100])
     fake = ctypes.c_void_p(16)
     pc = c.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
-    m = mf.MfBsrMap(2, 32, 4, 100, 10, 8, 8, 8, 8, 8, 8)
+    m = mf.MfBsrMap(2, 32, 4, 100, 10, 8, 8, 8, 8, 8, 8, None)
     f = lib.mf_apply_translated
     assert f(None, ctypes.byref(m), fake, 4, fake, 3, 64, pc, fake, 1, 1, fake, fake, 1 << 40) == mf.MF_ERR_INVALID_ARG
     assert f(None, ctypes.byref(m), fake, 4, fake, 2, 80, pc, fake, 1, 1, fake, fake, 1 << 40) == mf.MF_ERR_UNSUPPORTED
@@ -102,6 +102,22 @@ def test_apply_and_dense_reject_bad_arguments(lib):
     assert g(None, fake, fake, fake, 0, 6, 4, 64, pc, fake, 1, None, fake, fake, 1 << 40) == mf.MF_ERR_INVALID_ARG
     assert g(None, fake, fake, fake, 0, 4, 4, 64, pc, fake, 1, None, fake, fake, 10) == mf.MF_ERR_WORKSPACE
     assert lib.mf_read_status(None, None, None) == mf.MF_ERR_INVALID_ARG
+
+
+def test_prefix_dedupe_rejects_bad_arguments(lib):
+    c = cu([100, 60])
+    fake = ctypes.c_void_p(16)
+    pc = c.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    need = lib.mf_prefix_dedupe_workspace_bytes(pc, 2, 32)
+    assert need > 0
+    assert lib.mf_prefix_dedupe_workspace_bytes(pc, 2, 48) == 0
+    f = lib.mf_prefix_dedupe
+    assert f(None, fake, fake, 0, None, fake, 2, 4, 64, 32, fake, fake, need) == mf.MF_ERR_INVALID_ARG
+    assert f(None, fake, fake, 0, pc, fake, 2, 0, 64, 32, fake, fake, need) == mf.MF_ERR_INVALID_ARG
+    assert f(None, fake, fake, 7, pc, fake, 2, 4, 64, 32, fake, fake, need) == mf.MF_ERR_UNSUPPORTED
+    assert f(None, fake, fake, 0, pc, fake, 2, 4, 96, 32, fake, fake, need) == mf.MF_ERR_UNSUPPORTED
+    assert f(None, fake, fake, 0, pc, fake, 2, 4, 64, 32, None, fake, need) == mf.MF_ERR_INVALID_ARG
+    assert f(None, fake, fake, 0, pc, fake, 2, 4, 64, 32, fake, fake, need - 1) == mf.MF_ERR_WORKSPACE
 
 
 def test_status_strings(lib):

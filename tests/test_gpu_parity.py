@@ -4,6 +4,8 @@ Small cases run the whole oracle; full-size workloads run the whole HIP path at
 the benchmark's launch configuration and compare sampled block-rows the oracle
 can compute one by one.  Comparison rules are in parity_util.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -243,3 +245,104 @@ def test_dense_attention(gpu, lens, Hq, Hkv, d, dt):
         a, L = orc.seqs(wl.cu_seqlens)[s]
         if L:
             assert rel_frob(O[h, a:a + L], ref) <= OUT_RFROB
+
+
+# ---------------------------------------------------------------------------
+# shared-prefix block-rows (MapFlow §5.3)
+# ---------------------------------------------------------------------------
+
+def _multiturn(lens, dt="bf16", Hs=4, Ht=6, Hkv=3, seed=None):
+    s = dataclasses.replace(wlmod.SPECS[5], Hs=Hs, Ht=Ht, Hkv=Hkv, w_var=1.0 / Hs, qk_dtype=dt)
+    return wlmod.make_workload(s, seed=seed, lens=lens)
+
+
+@pytest.mark.parametrize("dt,B", [("bf16", 64), ("fp32", 32), ("bf16", 128)])
+def test_prefix_dedupe_alias_exact(gpu, dt, B):
+    """The device alias table equals the oracle's (direct array comparison), entry
+    for entry."""
+    wl = _multiturn([300, 520, 64, 130, 700, 300, 1], dt=dt, Hs=3)
+    q, k = to_dev_qk(wl, gpu)
+    got = mf.mf_prefix_dedupe(q, k, wl.cu_seqlens, B).cpu().numpy()
+    want = orc.prefix_alias(wl.q, wl.k, wl.cu_seqlens, B)
+    say(f"dedupe {dt} B={B}: {int((want != np.arange(len(want))).sum())} shared of {len(want)}")
+    assert got.tolist() == want.tolist()
+
+
+def _resolved_equal(m0, m1, alias, Hs):
+    """Every BSR row of the deduplicated map, read through its alias, equals the
+    plain map's row bit for bit (kept blocks, tiles); kept masses are equal."""
+    NBR = m0.num_block_rows
+    rp0, rp1 = m0.row_ptr.cpu().numpy(), m1.row_ptr.cpu().numpy()
+    ci0, ci1 = m0.col_idx.cpu().numpy(), m1.col_idx.cpu().numpy()
+    t0 = m0.tiles.view(torch.int16).cpu().numpy()
+    t1 = m1.tiles.view(torch.int16).cpu().numpy()
+    for h in range(Hs):
+        for gr in range(NBR):
+            r0, r1 = h * NBR + gr, h * NBR + int(alias[gr])
+            a0, b0, a1, b1 = rp0[r0], rp0[r0 + 1], rp1[r1], rp1[r1 + 1]
+            assert ci0[a0:b0].tolist() == ci1[a1:b1].tolist(), (h, gr)
+            assert np.array_equal(t0[a0:b0], t1[a1:b1]), (h, gr)
+            if int(alias[gr]) != gr:
+                assert rp1[h * NBR + gr + 1] == rp1[h * NBR + gr]  # no tiles of its own
+    assert torch.equal(m0.kept_mass, m1.kept_mass)
+
+
+def test_dedupe_map_and_output_equal_plain(gpu):
+    """Compressing with the alias table gives the same map, read through the
+    aliases, and the same translated output bit for bit, with fewer tiles."""
+    wl = _multiturn([600, 1000, 130, 900, 420], Hs=4, Ht=6, Hkv=3)
+    B = wl.spec.B
+    q, k = to_dev_qk(wl, gpu)
+    m0 = mf.mf_compress_topp(q, k, wl.cu_seqlens, B, wl.spec.p, wl.bias())
+    alias = mf.mf_prefix_dedupe(q, k, wl.cu_seqlens, B)
+    m1 = mf.mf_compress_topp(q, k, wl.cu_seqlens, B, wl.spec.p, wl.bias(), row_alias=alias)
+    (st0, n0), (st1, n1) = mf.mf_read_status(m0), mf.mf_read_status(m1)
+    assert st0 == mf.MF_OK and st1 == mf.MF_OK
+    a = alias.cpu().numpy()
+    shared = int((a != np.arange(len(a))).sum())
+    say(f"dedupe: {shared} of {len(a)} block-rows shared, tiles {n0} -> {n1}")
+    assert shared > 0 and n1 < n0
+    _resolved_equal(m0, m1, a, 4)
+    Wt, vd = torch.from_numpy(wl.W).to(gpu), to_dev_v(wl, gpu)
+    O0 = mf.mf_apply_translated(m0, Wt, vd, wl.cu_seqlens)
+    O1 = mf.mf_apply_translated(m1, Wt, vd, wl.cu_seqlens)
+    assert torch.equal(O0, O1)
+
+
+def test_dedupe_full_size_multiturn(gpu):
+    """Workload 5 at full size: the alias table is exactly the generator's planted
+    structure (full block-rows inside each sequence's copied prefix share sequence
+    0's), the deduplicated map equals the plain one through the aliases on sampled
+    rows, and the output is bitwise the same."""
+    wl = wlmod.make_config(5)
+    B, Hs = wl.spec.B, wl.spec.Hs
+    q, k = to_dev_qk(wl, gpu)
+    alias = mf.mf_prefix_dedupe(q, k, wl.cu_seqlens, B)
+    rows = orc.block_rows(wl.cu_seqlens, B)
+    first = np.concatenate([[0], np.cumsum([orc.nblocks(L, B) for L in wl.lens])])
+    expect = np.arange(len(rows))
+    for g, (s, I) in enumerate(rows):
+        if s > 0 and (I + 1) * B <= wl.prefix[s]:
+            expect[g] = first[0] + I
+    a = alias.cpu().numpy()
+    assert a.tolist() == expect.tolist()
+    m0 = mf.mf_compress_topp(q, k, wl.cu_seqlens, B, wl.spec.p, wl.bias())
+    m1 = mf.mf_compress_topp(q, k, wl.cu_seqlens, B, wl.spec.p, wl.bias(), row_alias=alias)
+    (st0, n0), (st1, n1) = mf.mf_read_status(m0), mf.mf_read_status(m1)
+    assert st0 == mf.MF_OK and st1 == mf.MF_OK
+    say(f"full workload 5: {int((a != np.arange(len(a))).sum())} of {len(a)} block-rows shared, tiles {n0} -> {n1}")
+    assert torch.equal(m0.kept_mass, m1.kept_mass)
+    rp0, rp1 = m0.row_ptr.cpu().numpy(), m1.row_ptr.cpu().numpy()
+    NBR = m0.num_block_rows
+    for gr in list(range(0, NBR, 37)) + [NBR - 1]:
+        for h in (0, Hs - 1):
+            r0, r1 = h * NBR + gr, h * NBR + int(a[gr])
+            n = rp0[r0 + 1] - rp0[r0]
+            assert n == rp1[r1 + 1] - rp1[r1]
+            assert torch.equal(m0.col_idx[rp0[r0]:rp0[r0] + n], m1.col_idx[rp1[r1]:rp1[r1] + n])
+            assert torch.equal(m0.tiles[rp0[r0]:rp0[r0] + n].view(torch.int16),
+                               m1.tiles[rp1[r1]:rp1[r1] + n].view(torch.int16))
+    Wt, vd = torch.from_numpy(wl.W).to(gpu), to_dev_v(wl, gpu)
+    O0 = mf.mf_apply_translated(m0, Wt, vd, wl.cu_seqlens)
+    O1 = mf.mf_apply_translated(m1, Wt, vd, wl.cu_seqlens)
+    assert torch.equal(O0, O1)

@@ -351,3 +351,98 @@ def test_workload_generator():
     w4W = wlmod.make_workload(wlmod.SPECS[4], lens=[128]).W
     assert ((w4W != 0).sum(axis=1) == 4).all() and np.allclose(w4W.sum(axis=1), 1.0, atol=1e-6)
     assert (w4W >= 0).all()
+
+
+# ---------------------------------------------------------------------------
+# shared prefixes (MapFlow §5.3, §2.3)
+# ---------------------------------------------------------------------------
+
+def test_prefix_alias_matches_planted_prefixes():
+    """The multi-turn generator copies the first P_s = min(L_s // 2, L_0) tokens of
+    sequence 0 into sequence s (q, k, v, every head); the rest is fresh noise. So
+    exactly the full block-rows (I + 1) * B <= P_s of s > 0 share sequence 0's
+    block-row I. Catches: comparing the wrong token range, aliasing partial blocks,
+    aliasing across different block indices, or picking a later sequence."""
+    wl = wlmod.small_variant(5, [300, 520, 64, 130, 700, 300], Hs=3, Ht=3, Hkv=3)
+    B = 32
+    cu, lens = wl.cu_seqlens, wl.lens
+    rows = orc.block_rows(cu, B)
+    first = np.concatenate([[0], np.cumsum([orc.nblocks(L, B) for L in lens])])
+    expect = np.arange(len(rows))
+    for g, (s, I) in enumerate(rows):
+        if s > 0 and (I + 1) * B <= wl.prefix[s]:
+            expect[g] = first[0] + I
+    got = orc.prefix_alias(wl.q, wl.k, cu, B)
+    assert got.tolist() == expect.tolist()
+    # sequence 5 repeats sequence 0's length and prefix rule; still sequence 0 first
+    assert any(got[first[5] + I] == I for I in range(3))
+
+
+def _bf_alias(q, k, cu, B):
+    """Pure-Python brute force: compare the token lists of every prefix directly."""
+    rows = orc.block_rows(cu, B)
+    idx = {r: g for g, r in enumerate(rows)}
+    out = []
+    for g, (s, I) in enumerate(rows):
+        a, L = int(cu[s]), int(cu[s + 1] - cu[s])
+        n = (I + 1) * B
+        hit = g
+        if n <= L:
+            mine = [(q[h][a + t].tolist(), k[h][a + t].tolist()) for h in range(q.shape[0]) for t in range(n)]
+            for s2 in range(s):
+                a2, L2 = int(cu[s2]), int(cu[s2 + 1] - cu[s2])
+                if n > L2:
+                    continue
+                other = [(q[h][a2 + t].tolist(), k[h][a2 + t].tolist()) for h in range(q.shape[0]) for t in range(n)]
+                if mine == other:
+                    hit = idx[(s2, I)]
+                    break
+        out.append(hit)
+    return out
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_prefix_alias_bruteforce(seed):
+    """Tiny random packs with planted repeats: a sequence that repeats another's
+    prefix exactly, one that differs in a single element of one head (q or k), one
+    whose repeated part ends inside a block, and a sequence repeated whole. Catches:
+    ignoring k, ignoring a head, off-by-one block coverage."""
+    rng = np.random.default_rng(seed)
+    B, Hs, d = 4, 2, 3
+    lens = [13, 13, 11, 9, 16, 13]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    q = rng.standard_normal((Hs, T, d)).astype(np.float32)
+    k = rng.standard_normal((Hs, T, d)).astype(np.float32)
+    def copy(dst, src, n):
+        for x in (q, k):
+            x[:, cu[dst]:cu[dst] + n] = x[:, cu[src]:cu[src] + n]
+    copy(1, 0, 13)          # whole repeat of sequence 0
+    copy(2, 0, 10)          # repeat ends inside block 2 (tokens 8..11)
+    copy(3, 0, 9)
+    k[1, cu[3] + 5, 2] += 1.0  # one element of one head's k differs inside block 1
+    copy(4, 0, 12)
+    copy(5, 4, 13)          # repeats sequence 4, whose first 12 tokens repeat 0
+    got = orc.prefix_alias(q, k, cu, B).tolist()
+    assert got == _bf_alias(q, k, cu, B)
+    assert got != list(range(len(got)))  # something is shared
+
+
+def test_shared_block_rows_compress_identically():
+    """The reason sharing is allowed: a full block-row with the same prefix as an
+    earlier one has the same masses, kept set, probabilities and kept mass (the
+    offsets are measured from each sequence start). Catches: a bias or causal mask
+    that depends on absolute token positions."""
+    wl = wlmod.small_variant(5, [300, 520, 130], Hs=2, Ht=2, Hkv=2)
+    B = 32
+    alias = orc.prefix_alias(wl.q, wl.k, wl.cu_seqlens, B)
+    rows = orc.block_rows(wl.cu_seqlens, B)
+    pairs = [(rows[g], rows[int(a)]) for g, a in enumerate(alias) if a != g]
+    assert pairs
+    res = orc.compress(wl.q, wl.k, wl.cu_seqlens, B, 0.9, wl.bias(),
+                       rows=sorted({r for pr in pairs for r in pr}))
+    for (s, I), (s2, I2) in pairs:
+        for h in range(2):
+            a, b = res[(h, s, I)], res[(h, s2, I2)]
+            assert a.kept == b.kept
+            assert np.array_equal(a.P, b.P) and np.array_equal(a.kmass, b.kmass)
