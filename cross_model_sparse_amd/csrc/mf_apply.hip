@@ -380,7 +380,7 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(4))) void
   const int ga = row_alias ? row_alias[gr] : gr;
   const int grm = (ga >= 0 && ga < NBR) ? ga : gr;
   const int ns = row_sources<C::NT>(mp, W, t, Hs, row_ptr, NBR, grm, tid);
-  if (ns > 4) return;  // handled by k_apply_many
+  if (ns > 4) return;  // handled by k_apply_mix
   row_maps_fill<B, C::NT>(mp, ns, row_ptr, col_idx, capacity, kept_mass, T, NBR, grm, tok0, I, L,
                           (n + 31) / 32, renorm, tid);
 
@@ -525,136 +525,311 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(4))) void
 }
 
 // ---------------------------------------------------------------------------
-// k_apply_many: targets with more than four sources (dense head mixing).  One
-// work-group per (target, query block), one wave per 16 query rows; per key
-// block and 32-key chunk, the sources are mixed four at a time.
+// k_apply_mix: targets with more than four sources (dense head mixing).
+//
+// One work-group per (query block, group of G consecutive targets); one wave
+// per 16 query rows, for all G targets.  Every source tile chunk (16 rows x 32
+// keys, one 1 KB fragment block) is loaded once per work-group and mixed into
+// the G translated rows.  Sources go two at a time: v_perm_b32 pairs their e-th
+// elements into one bf16 pair [P1[e], P2[e]], and one v_dot2 with the
+// coefficient pair [c1, c2] adds both products, so every instruction does two
+// multiply-adds and the pairing is shared by the G targets.  The coefficients
+// are c = W[t,h] / kmass_h[i] (bf16).
+//
+// Per key block of the union, the block's V tiles (one per distinct V head of
+// the group) load into LDS while the first 32-key chunk is mixed; then a full
+// drain and a barrier; then each chunk's bf16 mix is multiplied with V on MFMA
+// right after it is built; a barrier frees the V buffer for the next block.
+// Within a chunk, the next pair of source chunks loads while the current one
+// is mixed.
 // ---------------------------------------------------------------------------
 template <int B, int D>
-struct ApplyManyCfg {
-  static constexpr int NW = B / 16;                // waves per work-group, 16 rows each
+struct ApplyMixCfg {
+  static constexpr int G = (4 * D * B * 2 <= 64 * 1024) ? 4 : 2;  // targets per work-group
+  static constexpr int NW = B / 16;                 // waves, 16 rows each
   static constexpr int NT = NW * 64;
-  static constexpr int KC = B / 32;                // 32-key chunks per key block
+  static constexpr int KC = B / 32;                 // 32-key chunks per key block
   static constexpr int VBYTES = D * B * 2;
-  static constexpr int VINST = VBYTES / 1024 / NW; // 1 KB direct loads per wave per tile
+  static constexpr int VINST = VBYTES / 1024 / NW;  // 1 KB direct loads per wave per V tile
+  static constexpr int SB = 2;                      // sources per load batch (one pair)
   static_assert(VINST * 1024 * NW == VBYTES, "V tile must split into 1 KB wave loads");
+  static_assert(G * VBYTES <= 64 * 1024, "V buffers must stay in the first 64 KB of LDS");
 };
+constexpr int kMixMaxSources = 128;
+
+// Dynamic LDS of k_apply_mix (byte offsets): src[Hs] int32, rbase[Hs] int64,
+// wtab[Hs][4] fp32 (weight of each source for each target of the group),
+// bm[Hs][nbw], pc[Hs][nbw], uni[nbw], rtab[Hs][B] fp32 (1 / kept mass of each
+// row, 0 where none), blist[nbw * 32], counters.
+inline size_t mix_smem(int B, int Hs, int nbw) {
+  size_t s = (size_t)Hs * (4 + 8 + 16);
+  s += (size_t)Hs * nbw * 8 + (size_t)nbw * 4;
+  s += (size_t)Hs * B * 4;
+  s += (size_t)nbw * 32 * 4;
+  s += 64 + 64;
+  return s;
+}
 
 template <int B, int D>
-__global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(4))) void k_apply_many(
+__global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(2))) void k_apply_mix(
     const int64_t *__restrict__ row_ptr, const int32_t *__restrict__ col_idx,
     const uint16_t *__restrict__ tiles, const float *__restrict__ kept_mass, int32_t Hs,
     int32_t NBR, int64_t T, const float *__restrict__ W, int32_t Ht, int32_t grp,
     const uint16_t *__restrict__ vt, const RowInfo *__restrict__ rows,
     const int32_t *__restrict__ sched, int32_t nbw, int64_t capacity, int32_t renorm,
     float *__restrict__ o, const int32_t *__restrict__ row_alias) {
-  using C = ApplyManyCfg<B, D>;
-  constexpr int KC = C::KC;
-  __shared__ __attribute__((aligned(16))) char vA[C::VBYTES];
-  __shared__ __attribute__((aligned(16))) char vB[C::VBYTES];
+  using C = ApplyMixCfg<B, D>;
+  constexpr int G = C::G, KC = C::KC, SB = C::SB;
+  __shared__ __attribute__((aligned(16))) char vbuf[G * C::VBYTES];
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const RowMaps mp = row_maps(smem, Hs, nbw, B);
+  const int o_src = 0;
+  const int o_rbase = (o_src + Hs * 4 + 7) & ~7;
+  const int o_wt = o_rbase + Hs * 8;
+  const int o_bm = o_wt + Hs * 16;
+  const int o_pc = o_bm + Hs * nbw * 4;
+  const int o_uni = o_pc + Hs * nbw * 4;
+  const int o_rt = o_uni + nbw * 4;
+  const int o_bl = o_rt + Hs * B * 4;
+  const int o_misc = o_bl + nbw * 32 * 4;
+  int32_t *src = reinterpret_cast<int32_t *>(smem + o_src);
+  int64_t *rbase = reinterpret_cast<int64_t *>(smem + o_rbase);
+  float *wtab = reinterpret_cast<float *>(smem + o_wt);
+  uint32_t *bm = reinterpret_cast<uint32_t *>(smem + o_bm);
+  int32_t *pc = reinterpret_cast<int32_t *>(smem + o_pc);
+  uint32_t *uni = reinterpret_cast<uint32_t *>(smem + o_uni);
+  float *rtab = reinterpret_cast<float *>(smem + o_rt);
+  int32_t *blist = reinterpret_cast<int32_t *>(smem + o_bl);
+  int32_t *misc = reinterpret_cast<int32_t *>(smem + o_misc);  // [0] ns, [1..G] active
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m16 = lane & 15, kg = lane >> 4;
-  int pos, t;
-  xcd_map(Ht, pos, t);
+  const int ngrp = (Ht + G - 1) / G;
+  // work-group id -> (schedule position, target group), XCD-aware as in k_apply4
+  const int x = blockIdx.x % kXcds, kx = blockIdx.x / kXcds;
+  const int round = kx / ngrp, tg = kx % ngrp;
+  const int pos = round * kXcds + ((round & 1) ? (kXcds - 1 - x) : x);
   if (pos >= NBR) return;
   const int gr = sched[pos];
   const RowInfo ri = rows[gr];
   const int I = ri.blk, L = ri.len;
   const int n = I + 1;
-  const int g = t / grp;
   const int64_t tok0 = (int64_t)ri.start;
   const int64_t tpad = (int64_t)NBR * B;
-
-  // BSR row of this block-row: its own, or that of the earlier block-row it
-  // shares (tiles and kept masses are equal; V and O stay this row's own)
   const int ga = row_alias ? row_alias[gr] : gr;
-  const int grm = (ga >= 0 && ga < NBR) ? ga : gr;
-  const int ns = row_sources<C::NT>(mp, W, t, Hs, row_ptr, NBR, grm, tid);
-  if (ns <= 4) return;  // handled by k_apply4
-  row_maps_fill<B, C::NT>(mp, ns, row_ptr, col_idx, capacity, kept_mass, T, NBR, grm, tok0, I, L,
-                          (n + 31) / 32, renorm, tid);
-  auto next_J = [&](int from) -> int { return union_next(mp, n, from); };
-  auto tile_of = [&](int q, int J) -> int64_t { return tile_index(mp, q, J, capacity); };
-  const uint16_t *vtg = vt + (int64_t)g * D * tpad;
-  auto dma_v = [&](char *dstbuf, int J) {
-    dma_v_tile<B, D, C::VINST>(dstbuf, vtg, tpad, (int64_t)(gr - I + J) * B, wave, lane);
-  };
+  const int grm = (ga >= 0 && ga < NBR) ? ga : gr;  // BSR row (shared block-rows)
+  const int t0 = tg * G;
 
-  // lane row: wave * 16 + m16; keys of chunk kc: kc * 32 + 8 * kg + e.  The
-  // wave's 16 rows x 32 keys of chunk kc are one contiguous 1 KB block of the
-  // fragment-ordered tile, lane l's 16 bytes at l * 16.
-  const int r0 = wave * 16 + m16;
-  const uint16_t *rowbase = tiles + wave * KC * 512 + lane * 8;
-  f32x4 acc[D / 16];
-#pragma unroll
-  for (int nb = 0; nb < D / 16; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // translated row chunk (bf16) times the staged V tile
-  auto finish_chunk = [&](float (&mix)[8], const char *vl, int kc) {
-    u32x4 a;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) a[e] = pack_bf16x2(mix[2 * e], mix[2 * e + 1]);
-#pragma unroll
-    for (int nb = 0; nb < D / 16; ++nb) {
-      const u32x4 b = v_frag<B>(vl, nb * 16 + m16, kc * 4 + kg);
-      acc[nb] = mfma16_bf16(as_bf16x8(a), as_bf16x8(b), acc[nb]);
+  // ---- set-up: active targets, source union, weights, kept bitmaps ---------
+  if (tid == 0) {
+    int act[G];
+    for (int g = 0; g < G; ++g) {
+      int cnt = 0;
+      if (t0 + g < Ht)
+        for (int h = 0; h < Hs; ++h) cnt += W[(int64_t)(t0 + g) * Hs + h] != 0.f;
+      act[g] = cnt > 4;  // targets with at most four sources are k_apply4's
+      misc[1 + g] = act[g];
     }
-  };
-  auto mix_src = [&](float (&mix)[8], const u32x4 &v, uint32_t c) {
-    const uint32_t c_lo = c, c_hi = c << 16;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) mix_word(mix[2 * e], mix[2 * e + 1], v[e], c_lo, c_hi);
-  };
-  const uint16_t *coef = mp.coef;
+    int ns = 0;
+    for (int h = 0; h < Hs; ++h) {
+      bool any = false;
+      float w[G];
+      for (int g = 0; g < G; ++g) {
+        w[g] = act[g] ? W[(int64_t)(t0 + g) * Hs + h] : 0.f;
+        any |= w[g] != 0.f;
+      }
+      if (any) {
+        src[ns] = h;
+        rbase[ns] = row_ptr[(int64_t)h * NBR + grm];
+        for (int g = 0; g < G; ++g) wtab[ns * 4 + g] = w[g];
+        for (int g = G; g < 4; ++g) wtab[ns * 4 + g] = 0.f;
+        ++ns;
+      }
+    }
+    misc[0] = ns;
+  }
+  for (int i = tid; i < Hs * nbw; i += C::NT) bm[i] = 0u;
+  __syncthreads();
+  const int ns = __builtin_amdgcn_readfirstlane(misc[0]);
+  if (ns == 0) return;
+  for (int q = 0; q < ns; ++q) {
+    // entries past the capacity of an overflowed map are treated as missing
+    const int64_t b0 = rbase[q], e0 = min(row_ptr[(int64_t)src[q] * NBR + grm + 1], capacity);
+    for (int64_t idx = b0 + tid; idx < e0; idx += C::NT) {
+      const int J = col_idx[idx];
+      atomicOr(&bm[q * nbw + (J >> 5)], 1u << (J & 31));
+    }
+  }
+  for (int idx = tid; idx < ns * B; idx += C::NT) {
+    const int q = idx / B, il = idx % B;
+    const int ip = I * B + il;
+    float r = 0.f;
+    if (ip < L) {
+      if (renorm) {
+        const float km = kept_mass[(int64_t)src[q] * T + tok0 + ip];
+        r = km > 0.f ? 1.f / km : 0.f;
+      } else {
+        r = 1.f;
+      }
+    }
+    rtab[q * B + il] = r;
+  }
+  __syncthreads();
+  const int nw_row = (n + 31) / 32;
+  for (int q = tid; q < ns; q += C::NT) {
+    int run = 0;
+    for (int w = 0; w < nw_row; ++w) {
+      pc[q * nbw + w] = run;
+      run += __popc(bm[q * nbw + w]);
+    }
+  }
+  if (tid < nw_row) {
+    uint32_t u = 0u;
+    for (int q = 0; q < ns; ++q) u |= bm[q * nbw + tid];
+    uni[tid] = u;
+  }
+  __syncthreads();
+  // union block list
+  for (int J = tid; J < n; J += C::NT) {
+    const uint32_t w = uni[J >> 5];
+    if (!((w >> (J & 31)) & 1u)) continue;
+    int k = __popc(w & ((1u << (J & 31)) - 1u));
+    for (int i = 0; i < (J >> 5); ++i) k += __popc(uni[i]);
+    blist[k] = J;
+  }
+  int nblk = 0;
+  for (int i = 0; i < nw_row; ++i) nblk += __popc(uni[i]);
+  __syncthreads();
+  nblk = __builtin_amdgcn_readfirstlane(nblk);
 
-  int J = next_J(0);
-  if (J >= 0) dma_v(vA, J);
-  int buf = 0;
-  while (J >= 0) {
-    const int Jn = next_J(J + 1);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (Jn >= 0) dma_v(buf ? vA : vB, Jn);
-    const char *vl = buf ? vB : vA;
-    // many sources: chunk by chunk, four sources at a time
+  bool act[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) act[g] = misc[1 + g] != 0;
+  const int gv0 = t0 / grp;                       // V head of the group's first target
+  int nvh = 0;                                    // distinct V heads of the group
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+    if (t0 + g < Ht) nvh = (t0 + g) / grp - gv0 + 1;
+
+  const int r0 = wave * 16 + m16;                 // lane row inside the block
+  const int loff = (wave * KC * 64 + lane) * 8;   // lane's 16 bytes of chunk 0 (elements)
+  f32x4 acc[G][D / 16];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int nb = 0; nb < D / 16; ++nb) acc[g][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int kb = 0; kb < nblk; ++kb) {
+    const int J = __builtin_amdgcn_readfirstlane(blist[kb]);
+    // tile index of every source at J, lane u holding sources u and u + 64
+    int ti[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int u = lane + 64 * hh;
+      int v = -1;
+      if (u < ns) {
+        const uint32_t word = bm[u * nbw + (J >> 5)];
+        if ((word >> (J & 31)) & 1u) {
+          const int64_t tix = rbase[u] + pc[u * nbw + (J >> 5)] + __popc(word & ((1u << (J & 31)) - 1u));
+          if (tix < capacity) v = (int)tix;
+        }
+      }
+      ti[hh] = v;
+    }
+    auto tile_at = [&](int u) -> int {  // uniform
+      if (u >= ns) return -1;
+      return u < 64 ? __builtin_amdgcn_readlane(ti[0], u) : __builtin_amdgcn_readlane(ti[1], u - 64);
+    };
+    // V tiles of this block for every distinct V head of the group
+    const int64_t col0 = (int64_t)(gr - I + J) * B;
+    for (int vh = 0; vh < nvh; ++vh)
+      dma_v_tile<B, D, C::VINST>(vbuf + vh * C::VBYTES, vt + (int64_t)(gv0 + vh) * D * tpad, tpad,
+                                 col0, wave, lane);
+
+    u32x4 amix[G];
+    auto load_batch = [&](u32x4 (&d)[SB], int kc, int u0) {
+#pragma unroll
+      for (int e = 0; e < SB; ++e) {
+        const int t_ = tile_at(u0 + e);
+        d[e] = u32x4{0u, 0u, 0u, 0u};
+        if (t_ >= 0)
+          d[e] = *reinterpret_cast<const u32x4 *>(tiles + (int64_t)t_ * (B * B) + loff + kc * 512);
+      }
+    };
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
-      float mix[8];
+      float mx[G][8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) mix[e] = 0.f;
-      for (int q0 = 0; q0 < ns; q0 += 4) {
-        u32x4 va[4];
-        uint32_t cl[4];
+      for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          cl[u] = 0u;
-          const int q = q0 + u;
-          if (q >= ns) continue;
-          const int64_t ti = tile_of(q, J);
-          if (ti < 0) continue;
-          va[u] = *reinterpret_cast<const u32x4 *>(rowbase + ti * (int64_t)(B * B) + kc * 512);
-          cl[u] = (uint32_t)coef[q * B + r0];
+        for (int e = 0; e < 8; ++e) mx[g][e] = 0.f;
+      u32x4 cur[SB], nxt[SB];
+      load_batch(cur, kc, 0);
+      for (int u0 = 0; u0 < ns; u0 += SB) {
+        if (u0 + SB < ns) load_batch(nxt, kc, u0 + SB);
+#pragma unroll
+        for (int pr = 0; pr < SB / 2; ++pr) {
+          const int u1 = u0 + 2 * pr, u2 = u1 + 1;
+          const float ra = u1 < ns ? rtab[u1 * B + r0] : 0.f;
+          const float rb = u2 < ns ? rtab[u2 * B + r0] : 0.f;
+          uint32_t cp[G];
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            const float wa = u1 < ns ? wtab[u1 * 4 + g] : 0.f;
+            const float wb = u2 < ns ? wtab[u2 * 4 + g] : 0.f;
+            cp[g] = pack_bf16x2(wa * ra, wb * rb);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t lo = __builtin_amdgcn_perm(cur[2 * pr + 1][e], cur[2 * pr][e], 0x05040100u);
+            const uint32_t hi = __builtin_amdgcn_perm(cur[2 * pr + 1][e], cur[2 * pr][e], 0x07060302u);
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+              mx[g][2 * e] = __builtin_amdgcn_fdot2_f32_bf16(
+                  __builtin_bit_cast(bf16x2, lo), __builtin_bit_cast(bf16x2, cp[g]), mx[g][2 * e], false);
+              mx[g][2 * e + 1] = __builtin_amdgcn_fdot2_f32_bf16(
+                  __builtin_bit_cast(bf16x2, hi), __builtin_bit_cast(bf16x2, cp[g]), mx[g][2 * e + 1], false);
+            }
+          }
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (cl[u] != 0u) mix_src(mix, va[u], cl[u]);
+        for (int e = 0; e < SB; ++e) cur[e] = nxt[e];
       }
-      finish_chunk(mix, vl, kc);
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) amix[g][e] = pack_bf16x2(mx[g][2 * e], mx[g][2 * e + 1]);
+      if (kc == 0) {
+        // V tiles landed (direct-to-LDS loads: full drain) in every wave
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+      }
+#pragma unroll
+      for (int nb = 0; nb < D / 16; ++nb)
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const int vh = (t0 + g < Ht) ? (t0 + g) / grp - gv0 : 0;
+          const u32x4 bv = v_frag<B>(vbuf + vh * C::VBYTES, nb * 16 + m16, kc * 4 + kg);
+          acc[g][nb] = mfma16_bf16(as_bf16x8(amix[g]), as_bf16x8(bv), acc[g][nb]);
+        }
     }
-    buf ^= 1;
-    J = Jn;
+    // every wave's reads of V done before the next block's loads overwrite it
+    __syncthreads();
   }
 
-  float *ot = o + (int64_t)t * T * D;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int ip = I * B + wave * 16 + 4 * kg + r;
-    if (ip < L) {
-      float *dst = ot + (tok0 + ip) * D + m16;
+  for (int g = 0; g < G; ++g) {
+    if (!act[g]) continue;
+    float *ot = o + (int64_t)(t0 + g) * T * D;
 #pragma unroll
-      for (int nb = 0; nb < D / 16; ++nb) dst[nb * 16] = acc[nb][r];
+    for (int r = 0; r < 4; ++r) {
+      const int ip = I * B + wave * 16 + 4 * kg + r;
+      if (ip < L) {
+        float *dst = ot + (tok0 + ip) * D + m16;
+#pragma unroll
+        for (int nb = 0; nb < D / 16; ++nb) dst[nb * 16] = acc[g][nb][r];
+      }
     }
   }
 }
@@ -665,35 +840,39 @@ static mf_status launch_apply(hipStream_t s, const mf_bsr_map *map, const float 
                               float *o, void *ws, const VtWs &w) {
   const int nbw = (g.maxnb + 31) / 32 > 0 ? (g.maxnb + 31) / 32 : 1;
   const size_t smem = apply_smem(B, map->num_heads, nbw);
+  const size_t smem_mix = mix_smem(B, map->num_heads, nbw);
   // tile indices are held in int32; V rows are addressed with 32-bit byte
   // offsets d * NBR * B * 2
   if (map->capacity_tiles > INT32_MAX) return MF_ERR_UNSUPPORTED;
   if ((int64_t)D * g.NBR * B * 2 >= ((int64_t)1 << 31)) return MF_ERR_UNSUPPORTED;
-  const size_t vbufs = 2 * (size_t)B * D * 2;  // the two static V tile buffers
-  if (smem + vbufs > 160 * 1024) return MF_ERR_UNSUPPORTED;
+  if (map->num_heads > kMixMaxSources) return MF_ERR_UNSUPPORTED;
+  const size_t vbufs = 2 * (size_t)B * D * 2;  // the two static V tile buffers of k_apply4
+  const size_t vbufs_mix = (size_t)ApplyMixCfg<B, D>::G * B * D * 2;
+  if (smem + vbufs > 160 * 1024 || smem_mix + vbufs_mix > 160 * 1024) return MF_ERR_UNSUPPORTED;
   hipLaunchKernelGGL((k_vtranspose<B, D>), dim3(g.NBR, Hkv), dim3(256), 0, s,
                      reinterpret_cast<const uint16_t *>(v), g.T, at<RowInfo>(ws, w.rt.rows), g.NBR,
                      at<uint16_t>(ws, w.vt));
   if (hip_status() != MF_OK) return MF_ERR_HIP;
-  if (smem + vbufs > 64 * 1024) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&k_apply4<B, D>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess ||
-        hipFuncSetAttribute(reinterpret_cast<const void *>(&k_apply_many<B, D>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
-      return MF_ERR_HIP;
-  }
+  if (smem + vbufs > 64 * 1024 &&
+      hipFuncSetAttribute(reinterpret_cast<const void *>(&k_apply4<B, D>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
+    return MF_ERR_HIP;
+  if (smem_mix + vbufs_mix > 64 * 1024 &&
+      hipFuncSetAttribute(reinterpret_cast<const void *>(&k_apply_mix<B, D>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem_mix) != hipSuccess)
+    return MF_ERR_HIP;
   const int64_t npos = ((int64_t)g.NBR + kXcds - 1) / kXcds * kXcds;
-  // one launch per source-count class; a work-group whose target is of the other
-  // class returns right after reading its weight row
+  // one launch per source-count class; a work-group whose targets are all of
+  // the other class returns right after reading their weight rows
   hipLaunchKernelGGL((k_apply4<B, D>), dim3((unsigned)(npos * Ht)), dim3(Apply4Cfg<B, D>::NT),
                      smem, s, map->row_ptr, map->col_idx, map->tiles, map->kept_mass,
                      map->num_heads, g.NBR, g.T, W, Ht, Ht / Hkv, at<uint16_t>(ws, w.vt),
                      at<RowInfo>(ws, w.rt.rows), at<int32_t>(ws, w.rt.sched), nbw,
-                     map->capacity_tiles, renorm, o,
-                     map->row_alias);
+                     map->capacity_tiles, renorm, o, map->row_alias);
   if (hip_status() != MF_OK) return MF_ERR_HIP;
-  hipLaunchKernelGGL((k_apply_many<B, D>), dim3((unsigned)(npos * Ht)),
-                     dim3(ApplyManyCfg<B, D>::NT), smem, s, map->row_ptr, map->col_idx,
+  const int64_t ngrp = (Ht + ApplyMixCfg<B, D>::G - 1) / ApplyMixCfg<B, D>::G;
+  hipLaunchKernelGGL((k_apply_mix<B, D>), dim3((unsigned)(npos * ngrp)),
+                     dim3(ApplyMixCfg<B, D>::NT), smem_mix, s, map->row_ptr, map->col_idx,
                      map->tiles, map->kept_mass, map->num_heads, g.NBR, g.T, W, Ht, Ht / Hkv,
                      at<uint16_t>(ws, w.vt), at<RowInfo>(ws, w.rt.rows),
                      at<int32_t>(ws, w.rt.sched), nbw, map->capacity_tiles, renorm, o,
