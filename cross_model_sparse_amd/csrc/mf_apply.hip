@@ -540,7 +540,7 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(4))) void
 // the group) load into LDS while the first 32-key chunk is mixed; then a full
 // drain and a barrier; then each chunk's bf16 mix is multiplied with V on MFMA
 // right after it is built; a barrier frees the V buffer for the next block.
-// Within a chunk, the next pair of source chunks loads while the current one
+// Within a chunk, the next batch of source chunks loads while the current one
 // is mixed.
 // ---------------------------------------------------------------------------
 template <int B, int D>
@@ -551,7 +551,7 @@ struct ApplyMixCfg {
   static constexpr int KC = B / 32;                 // 32-key chunks per key block
   static constexpr int VBYTES = D * B * 2;
   static constexpr int VINST = VBYTES / 1024 / NW;  // 1 KB direct loads per wave per V tile
-  static constexpr int SB = 2;                      // sources per load batch (one pair)
+  static constexpr int SB = 4;                      // sources per load batch (two pairs)
   static_assert(VINST * 1024 * NW == VBYTES, "V tile must split into 1 KB wave loads");
   static_assert(G * VBYTES <= 64 * 1024, "V buffers must stay in the first 64 KB of LDS");
 };
