@@ -519,7 +519,7 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(4))) void
       if (ip < L) {
         float *dst = ot + (tok0 + ip) * D + m16;
 #pragma unroll
-        for (int nb = 0; nb < D / 16; ++nb) dst[nb * 16] = acc[h][nb][r];
+        for (int nb = 0; nb < D / 16; ++nb) __builtin_nontemporal_store(acc[h][nb][r], dst + nb * 16);
       }
     }
 }
@@ -828,7 +828,7 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(2))) void
       if (ip < L) {
         float *dst = ot + (tok0 + ip) * D + m16;
 #pragma unroll
-        for (int nb = 0; nb < D / 16; ++nb) dst[nb * 16] = acc[g][nb][r];
+        for (int nb = 0; nb < D / 16; ++nb) __builtin_nontemporal_store(acc[g][nb][r], dst + nb * 16);
       }
     }
   }

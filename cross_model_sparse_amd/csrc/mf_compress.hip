@@ -314,7 +314,9 @@ __device__ __forceinline__ void store_tile_rows(char *dst, const uint2 (&w)[B / 
       const u32x4 chunk = u32x4{s0[0], s1[0], s0[1], s1[1]};
       const int q = 2 * pr + hl;
       const int off = (((i_loc >> 4) * (B / 32) + mb) * 64 + q * 16 + (i_loc & 15)) * 16;
-      *reinterpret_cast<u32x4 *>(dst + off) = chunk;
+      // streaming store: the map is not read again by this pass, and letting
+      // it allocate in L2 would evict the K rows other work-groups still read
+      __builtin_nontemporal_store(chunk, reinterpret_cast<u32x4 *>(dst + off));
     }
 }
 
