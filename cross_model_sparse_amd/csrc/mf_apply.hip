@@ -4,13 +4,13 @@
 //
 //   O_t[i,:] = sum_h W[t,h] sum_{J kept by h} sum_{j in J} (A_h[i,j] / kmass_h[i]) V_g(t)[j,:]
 //
-// One work-group per (target head, query block); one wave per 32 query rows.
-// Per key block J in the union of the sources' kept sets, each lane rebuilds its
-// row of the translated tile  A~_t[i, J] = sum_h c_h[i] A_h[i, J]  in fp32
-// registers straight from the bf16 tiles (c_h[i] = W[t,h] / kmass_h[i]),
-// rounds it to bf16 and feeds it as the A operand of a 32x32x16 MFMA against
-// V_g(t)[J] staged in LDS.  The translated map never leaves registers; nothing
-// of size L x L is written.
+// Per (target head, query block) and key block J in the union of the sources'
+// kept sets, each lane rebuilds its row of the translated tile
+// A~_t[i, J] = sum_h c_h[i] A_h[i, J] in fp32 registers straight from the bf16
+// tiles (c_h[i] = W[t,h] / kmass_h[i]), rounds it to bf16 and feeds it as the A
+// operand of 16x16x32 MFMAs against V_g(t)[J] staged in LDS.  The translated
+// map never leaves registers; nothing of size L x L is written.  k_apply4 takes
+// targets with at most four sources, k_apply_mix the others.
 //
 // V is first copied into a transposed, block-padded layout Vt[g][d][NBR * B]
 // (k_vtranspose) so that the MFMA B operand (8 consecutive keys of one value
@@ -125,18 +125,22 @@ __device__ __forceinline__ RowMaps row_maps(char *smem, int Hs, int nbw, int B) 
 template <int NT>
 __device__ int row_sources(const RowMaps &m, const float *__restrict__ W, int t, int Hs,
                            const int64_t *__restrict__ row_ptr, int NBR, int gr, int tid) {
-  if (tid == 0) {
+  if (tid < 64) {
+    // wave 0 scans the weight row 64 heads at a time, compacting by ballot
     int ns = 0;
-    for (int h = 0; h < Hs; ++h) {
-      const float w = W[(int64_t)t * Hs + h];
+    for (int h0 = 0; h0 < Hs; h0 += 64) {
+      const int h = h0 + tid;
+      const float w = h < Hs ? W[(int64_t)t * Hs + h] : 0.f;
+      const uint64_t mask = wave_ballot(w != 0.f);
       if (w != 0.f) {
-        m.src[ns] = h;
-        m.wt[ns] = w;
-        m.rbase[ns] = row_ptr[(int64_t)h * NBR + gr];
-        ++ns;
+        const int q = ns + lanes_below(mask);
+        m.src[q] = h;
+        m.wt[q] = w;
+        m.rbase[q] = row_ptr[(int64_t)h * NBR + gr];
       }
+      ns += __popcll(mask);
     }
-    *m.nsrc = ns;
+    if (tid == 0) *m.nsrc = ns;
   }
   for (int i = tid; i < Hs * m.nbw; i += NT) m.bm[i] = 0u;
   __syncthreads();
@@ -620,32 +624,48 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(2))) void
   const int t0 = tg * G;
 
   // ---- set-up: active targets, source union, weights, kept bitmaps ---------
-  if (tid == 0) {
-    int act[G];
+  if (tid < 64) {
+    // wave 0, 64 heads at a time: source counts of the G targets (those with at
+    // most four sources are k_apply4's), then the union of the active targets'
+    // sources compacted by ballot in ascending head order
+    bool act[G];
+#pragma unroll
     for (int g = 0; g < G; ++g) {
       int cnt = 0;
       if (t0 + g < Ht)
-        for (int h = 0; h < Hs; ++h) cnt += W[(int64_t)(t0 + g) * Hs + h] != 0.f;
-      act[g] = cnt > 4;  // targets with at most four sources are k_apply4's
-      misc[1 + g] = act[g];
+        for (int h0 = 0; h0 < Hs; h0 += 64) {
+          const int h = h0 + tid;
+          cnt += __popcll(wave_ballot(h < Hs && W[(int64_t)(t0 + g) * Hs + h] != 0.f));
+        }
+      act[g] = cnt > 4;
     }
     int ns = 0;
-    for (int h = 0; h < Hs; ++h) {
-      bool any = false;
+    for (int h0 = 0; h0 < Hs; h0 += 64) {
+      const int h = h0 + tid;
       float w[G];
+      bool any = false;
+#pragma unroll
       for (int g = 0; g < G; ++g) {
-        w[g] = act[g] ? W[(int64_t)(t0 + g) * Hs + h] : 0.f;
+        w[g] = (act[g] && h < Hs) ? W[(int64_t)(t0 + g) * Hs + h] : 0.f;
         any |= w[g] != 0.f;
       }
+      const uint64_t mask = wave_ballot(any);
       if (any) {
-        src[ns] = h;
-        rbase[ns] = row_ptr[(int64_t)h * NBR + grm];
-        for (int g = 0; g < G; ++g) wtab[ns * 4 + g] = w[g];
-        for (int g = G; g < 4; ++g) wtab[ns * 4 + g] = 0.f;
-        ++ns;
+        const int q = ns + lanes_below(mask);
+        src[q] = h;
+        rbase[q] = row_ptr[(int64_t)h * NBR + grm];
+#pragma unroll
+        for (int g = 0; g < G; ++g) wtab[q * 4 + g] = w[g];
+#pragma unroll
+        for (int g = G; g < 4; ++g) wtab[q * 4 + g] = 0.f;
       }
+      ns += __popcll(mask);
     }
-    misc[0] = ns;
+    if (tid == 0) {
+      misc[0] = ns;
+#pragma unroll
+      for (int g = 0; g < G; ++g) misc[1 + g] = act[g];
+    }
   }
   for (int i = tid; i < Hs * nbw; i += C::NT) bm[i] = 0u;
   __syncthreads();

@@ -99,6 +99,16 @@ __device__ __forceinline__ float pair_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Wave-wide stream compaction: the mask of lanes with `pred` set, and this
+// lane's rank among them (number of set lanes below it).
+__device__ __forceinline__ uint64_t wave_ballot(bool pred) {
+  return __builtin_amdgcn_ballot_w64(pred);
+}
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
 // ---------------------------------------------------------------------------
 // Block-row table, built once per call from the device sequence offsets.
 // Global block-row gr -> (sequence, block index in the sequence), and a
