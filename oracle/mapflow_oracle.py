@@ -33,6 +33,9 @@ What it computes, and where that is stated:
   renorm divides each kept row by its kept mass and g(t) = floor(t * Hkv / Ht)
   picks the V head of target t.  With W = I this is the AttnCache reuse path
   (cached map times V; AttnCache guide, PyTorch prototype).
+* fp8 tiles (optional).  MapFlow §9 names quantised sparse maps as the way to
+  shrink them further; `codec="mxfp8"` in apply reads every kept tile through
+  the block-scaled E4M3 codec of oracle/mx_codec.py.
 * Dense attention for recomputed heads (MapFlow §4: the receiver computes its
   first r layers normally): O_h = A_h V_g(h).
 
@@ -45,6 +48,8 @@ import dataclasses
 from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
+
+from oracle import mx_codec
 
 AMBIGUITY_REL = 1e-5  # relative band around the top-p cut treated as a tie
 
@@ -313,10 +318,15 @@ def v_head(t: int, Ht: int, Hkv: int) -> int:
 
 
 def apply_row(src_rows: Dict[int, RowResult], W: np.ndarray, t: int, v_seq: np.ndarray,
-              B: int, renorm: bool = True) -> np.ndarray:
+              B: int, renorm: bool = True, codec: Optional[str] = None) -> np.ndarray:
     """O_t for one block-row: sum_h W[t,h] * sum_{J kept by h} (P^h / kmass^h) V[J].
 
-    src_rows: {h: RowResult of that source's block-row}; v_seq: [L, d] of V head g(t)."""
+    src_rows: {h: RowResult of that source's block-row}; v_seq: [L, d] of V head g(t).
+    codec "mxfp8": each kept B x B tile is first replaced by what the block-scaled
+    E4M3 tile codec (oracle.mx_codec) reads back; the kept mass stays that of the
+    unquantised probabilities."""
+    if codec not in (None, "mxfp8"):
+        raise ValueError(f"unknown tile codec {codec!r}")
     v = np.asarray(v_seq, dtype=np.float64)
     any_row = next(iter(src_rows.values()))
     out = np.zeros((len(any_row.rows), v.shape[1]), dtype=np.float64)
@@ -331,6 +341,8 @@ def apply_row(src_rows: Dict[int, RowResult], W: np.ndarray, t: int, v_seq: np.n
             scale = np.full(len(rr.rows), w)
         for J in rr.kept:
             blk = rr.P[:, J * B:(J + 1) * B]
+            if codec == "mxfp8":
+                blk = mx_codec.quantize(rr.tile(J, B))[:blk.shape[0], :blk.shape[1]]
             out += scale[:, None] * (blk @ v[J * B:J * B + blk.shape[1]])
     return out
 
@@ -338,7 +350,8 @@ def apply_row(src_rows: Dict[int, RowResult], W: np.ndarray, t: int, v_seq: np.n
 def apply(res: Dict[Tuple[int, int, int], RowResult], W: np.ndarray, v: np.ndarray,
           cu: np.ndarray, B: int, Hkv: int, renorm: bool = True,
           targets: Optional[Sequence[int]] = None,
-          rows: Optional[Sequence[Tuple[int, int]]] = None) -> Dict[Tuple[int, int, int], np.ndarray]:
+          rows: Optional[Sequence[Tuple[int, int]]] = None,
+          codec: Optional[str] = None) -> Dict[Tuple[int, int, int], np.ndarray]:
     """Translated retrieval for the given (target, (seq, block-row)) pairs.
 
     res must hold every source with a nonzero weight for those rows. v: [Hkv][T][d].
@@ -357,7 +370,7 @@ def apply(res: Dict[Tuple[int, int, int], RowResult], W: np.ndarray, v: np.ndarr
                 n = len(range(I * B, min((I + 1) * B, L)))
                 out[(t, s, I)] = np.zeros((n, v.shape[2]))
                 continue
-            out[(t, s, I)] = apply_row(src, W, t, v[g, a:a + L], B, renorm)
+            out[(t, s, I)] = apply_row(src, W, t, v[g, a:a + L], B, renorm, codec)
     return out
 
 
