@@ -324,12 +324,17 @@ __device__ __forceinline__ u32x4 v_frag(const char *vl, int d, int c) {
 // ---------------------------------------------------------------------------
 constexpr int cgcd(int a, int b) { return b == 0 ? a : cgcd(b, a % b); }
 
-template <int B, int D>
+template <int B, int D, int FMT>
 struct Apply4Cfg {
   static constexpr int RG = 1;                       // 16-row MFMA groups per wave
   static constexpr int NW = B / (16 * RG);           // waves
   static constexpr int NT = NW * 64;
   static constexpr int KC = B / 32;                  // 32-key chunks per key block
+  // a ring unit is one load per source: a 32-key chunk of bf16 (16 bytes per
+  // lane), or NP chunks of E4M3 codes (8 NP bytes per lane)
+  static constexpr int NP = (FMT == MF_TILE_MXFP8 && B >= 64) ? 2 : 1;
+  static constexpr int KU = KC / NP;                 // units per key block
+  static constexpr int64_t TBYTES = tile_bytes(B, FMT);
   static constexpr int VBYTES = D * B * 2;
   static constexpr int VINST = VBYTES / 1024 / NW;   // 1 KB direct loads per wave per V tile
   // Ring slots (chunks).  Two, i.e. one chunk ahead: about eight work-groups
@@ -338,27 +343,30 @@ struct Apply4Cfg {
   // (measured at L = 32K: L2 hit rate 54% with two slots, 12% with four, and
   // twice the fabric traffic); 32-row waves with more slots lose the same way.
   static constexpr int NR = 2;
-  static constexpr int LPC = 4 * RG;                 // tile loads per chunk: row groups x 4 sources
+  // loads per unit: row groups x 4 sources, plus 4 scale loads with a block's first unit
+  static constexpr int LPC = 4 * RG + (FMT == MF_TILE_MXFP8 ? 4 : 0);
   // key blocks per unrolled trip: ring slots and V buffers both return to their start
-  static constexpr int TB = (NR * 2 * KC / cgcd(NR, 2 * KC)) / KC;
+  static constexpr int TB = (NR * 2 * KU / cgcd(NR, 2 * KU)) / KU;
   // descriptor queue depth: blocks from the current one to the farthest prefetched
-  static constexpr int DQ = (KC - 1 + NR - 1) / KC + 1;
+  static constexpr int DQ = (KU - 1 + NR - 1) / KU + 1;
   static_assert(VINST * 1024 * NW == VBYTES, "V tile must split into 1 KB wave loads");
-  static_assert(TB % 2 == 0 && (TB * KC) % NR == 0, "trip must close the ring and V buffers");
+  static_assert(TB % 2 == 0 && (TB * KU) % NR == 0, "trip must close the ring and V buffers");
   static_assert((NR - 1) * LPC + VINST <= 63, "vmcnt range");
+  static_assert(FMT == MF_TILE_BF16 || RG == 1, "fp8 tiles take one row group per wave");
 };
 
 
-template <int B, int D>
+template <int B, int D, int FMT>
 __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(4))) void k_apply4(
     const int64_t *__restrict__ row_ptr, const int32_t *__restrict__ col_idx,
-    const uint16_t *__restrict__ tiles, const float *__restrict__ kept_mass, int32_t Hs,
+    const char *__restrict__ tiles, const float *__restrict__ kept_mass, int32_t Hs,
     int32_t NBR, int64_t T, const float *__restrict__ W, int32_t Ht, int32_t grp,
     const uint16_t *__restrict__ vt, const RowInfo *__restrict__ rows,
     const int32_t *__restrict__ sched, int32_t nbw, int64_t capacity, int32_t renorm,
     float *__restrict__ o, const int32_t *__restrict__ row_alias) {
-  using C = Apply4Cfg<B, D>;
-  constexpr int KC = C::KC, NR = C::NR, TB = C::TB, DQ = C::DQ;
+  using C = Apply4Cfg<B, D, FMT>;
+  constexpr int KU = C::KU, NP = C::NP, NR = C::NR, TB = C::TB, DQ = C::DQ;
+  constexpr bool FP8 = FMT == MF_TILE_MXFP8;
   // separate arrays, so the compiler can tell that direct loads into one never
   // alias reads of the other
   __shared__ __attribute__((aligned(16))) char vA[C::VBYTES];
@@ -416,19 +424,41 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(4))) void
     for (int u = 0; u < 4; ++u) {
       const int ti = __builtin_amdgcn_readfirstlane((int)ti4[u]);
       S.r[u] = __builtin_amdgcn_make_buffer_rsrc(
-          (void *)(tiles + (int64_t)(ti >= 0 ? ti : 0) * (B * B)), 0, ti >= 0 ? B * B * 2 : 0,
-          kBufferFlags);
+          (void *)(tiles + (int64_t)(ti >= 0 ? ti : 0) * C::TBYTES), 0,
+          ti >= 0 ? (int)C::TBYTES : 0, kBufferFlags);
     }
   };
-  // chunk kc of both row groups: the wave's 1 KB fragment blocks of row groups
-  // 2 * wave and 2 * wave + 1, lane l's 16 bytes at l * 16
-  const int voff = (RG * wave * KC * 64 + lane) * 16;
-  auto load_chunk = [&](u32x4 (&dst)[RG][4], const Src4 &S, int kc) {
+  // unit ku of the wave's row groups: bf16, the 1 KB fragment block (row group,
+  // chunk ku), lane l's 16 bytes at l * 16; fp8, the (row group, piece ku)
+  // block of 512 NP bytes, lane l's 8 NP bytes at l * 8 NP
+  const int voff = FP8 ? (wave * KU * 64 + lane) * 8 * NP : (RG * wave * KU * 64 + lane) * 16;
+  auto load_chunk = [&](u32x4 (&dst)[RG][4], const Src4 &S, int ku) {
 #pragma unroll
     for (int h = 0; h < RG; ++h)
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        dst[h][u] = __builtin_amdgcn_raw_buffer_load_b128(S.r[u], voff, (h * KC + kc) * 1024, 0);
+      for (int u = 0; u < 4; ++u) {
+        if constexpr (!FP8) {
+          dst[h][u] = __builtin_amdgcn_raw_buffer_load_b128(S.r[u], voff, (h * KU + ku) * 1024, 0);
+        } else if constexpr (NP == 2) {
+          dst[h][u] = __builtin_amdgcn_raw_buffer_load_b128(S.r[u], voff, ku * 1024, 0);
+        } else {
+          const auto d2 = __builtin_amdgcn_raw_buffer_load_b64(S.r[u], voff, ku * 512, 0);
+          dst[h][u] = u32x4{d2[0], d2[1], 0u, 0u};
+        }
+      }
+  };
+  // scale bytes of the lane's row (B/32 of them, one per chunk), fp8 only
+  const int soff_lane = (wave * 16 + m16) * (B / 32);
+  auto load_scales = [&](uint32_t (&sc)[4], const Src4 &S) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if constexpr (B == 128)
+        sc[u] = __builtin_amdgcn_raw_buffer_load_b32(S.r[u], soff_lane, B * B, 0);
+      else if constexpr (B == 64)
+        sc[u] = __builtin_amdgcn_raw_buffer_load_b16(S.r[u], soff_lane, B * B, 0);
+      else
+        sc[u] = __builtin_amdgcn_raw_buffer_load_b8(S.r[u], soff_lane, B * B, 0);
+    }
   };
 
   const uint16_t *vtg = vt + (int64_t)g * D * tpad;
@@ -442,16 +472,26 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(4))) void
 #pragma unroll
     for (int nb = 0; nb < D / 16; ++nb) acc[h][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // fp8: coefficients as fp32, scaled per chunk by the tile's block scale
+  float cf[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) cf[u] = __uint_as_float(clo[0][u] << 16);
+
   if (nblk > 0) {
     // queue of tile descriptors: S[k] for the (cur + k)-th union block
     Src4 S[DQ];
 #pragma unroll
     for (int k = 0; k < DQ; ++k) src4(S[k], k);
     u32x4 ring[NR][RG][4];
-    // prologue: the first V tile and chunks 0 .. NR-2
+    uint32_t sc[2][4];  // fp8 scale words of blocks with even / odd trip position
+    // prologue: the first V tile and units 0 .. NR-2
     dma_v(vA, blk_J(0));
 #pragma unroll
-    for (int p = 0; p < NR - 1; ++p) load_chunk(ring[p], S[p / KC], p % KC);
+    for (int p = 0; p < NR - 1; ++p) {
+      load_chunk(ring[p], S[p / KU], p % KU);
+      if constexpr (FP8)
+        if (p % KU == 0) load_scales(sc[(p / KU) & 1], S[p / KU]);
+    }
     int cur = 0;  // list position of the block being multiplied
     bool done = false;
     while (!done) {
@@ -472,34 +512,59 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(4))) void
         asm volatile("" ::: "memory");
         dma_v(vnxt, Jn >= 0 ? Jn : Jc);  // unconditional: static wait counts
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-          const int pc = tb * KC + kc;          // chunk position in the trip
-          const int pf = kc + NR - 1;           // prefetched chunk, relative to this block
-          load_chunk(ring[(pc + NR - 1) % NR], S[pf / KC], pf % KC);
-          // keep the prefetch ahead of this chunk's work (the scheduler would
+        for (int ku = 0; ku < KU; ++ku) {
+          const int pc = tb * KU + ku;          // unit position in the trip
+          const int pf = ku + NR - 1;           // prefetched unit, relative to this block
+          load_chunk(ring[(pc + NR - 1) % NR], S[pf / KU], pf % KU);
+          if constexpr (FP8)
+            if (pf % KU == 0) load_scales(sc[(tb + pf / KU) & 1], S[pf / KU]);
+          // keep the prefetch ahead of this unit's work (the scheduler would
           // otherwise sink it next to its first use)
           __builtin_amdgcn_sched_barrier(0);
           const u32x4(&cr)[RG][4] = ring[pc % NR];
-          u32x4 a[RG];
 #pragma unroll
-          for (int h = 0; h < RG; ++h) {
-            float mx[8];
+          for (int sub = 0; sub < NP; ++sub) {
+            const int kc = ku * NP + sub;       // 32-key chunk of the block
+            u32x4 a[RG];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) mx[e] = 0.f;
+            for (int h = 0; h < RG; ++h) {
+              float mx[8];
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
+              for (int e = 0; e < 8; ++e) mx[e] = 0.f;
+              if constexpr (!FP8) {
 #pragma unroll
-              for (int e = 0; e < 4; ++e)
-                mix_word(mx[2 * e], mx[2 * e + 1], cr[h][u][e], clo[h][u], clo[h][u] << 16);
+                for (int u = 0; u < 4; ++u)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) a[h][e] = pack_bf16x2(mx[2 * e], mx[2 * e + 1]);
-          }
+                  for (int e = 0; e < 4; ++e)
+                    mix_word(mx[2 * e], mx[2 * e + 1], cr[h][u][e], clo[h][u], clo[h][u] << 16);
+              } else {
+                // code_value * 2^(scale byte - 127), the scale folded into c
 #pragma unroll
-          for (int nb = 0; nb < D / 16; ++nb) {
-            const u32x4 bv = v_frag<B>(vcur, nb * 16 + m16, kc * 4 + kg);
+                for (int u = 0; u < 4; ++u) {
+                  const int sb = (int)((sc[tb & 1][u] >> (8 * kc)) & 0xffu);
+                  const float c = __builtin_amdgcn_ldexpf(cf[u], sb - 127);
 #pragma unroll
-            for (int h = 0; h < RG; ++h)
-              acc[h][nb] = mfma16_bf16(as_bf16x8(a[h]), as_bf16x8(bv), acc[h][nb]);
+                  for (int w = 0; w < 2; ++w) {
+                    const uint32_t codes = cr[h][u][2 * sub + w];
+                    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(codes, false);
+                    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(codes, true);
+                    mx[4 * w + 0] = fmaf(c, lo[0], mx[4 * w + 0]);
+                    mx[4 * w + 1] = fmaf(c, lo[1], mx[4 * w + 1]);
+                    mx[4 * w + 2] = fmaf(c, hi[0], mx[4 * w + 2]);
+                    mx[4 * w + 3] = fmaf(c, hi[1], mx[4 * w + 3]);
+                  }
+                }
+              }
+#pragma unroll
+              for (int e = 0; e < 4; ++e) a[h][e] = pack_bf16x2(mx[2 * e], mx[2 * e + 1]);
+            }
+#pragma unroll
+            for (int nb = 0; nb < D / 16; ++nb) {
+              const u32x4 bv = v_frag<B>(vcur, nb * 16 + m16, kc * 4 + kg);
+#pragma unroll
+              for (int h = 0; h < RG; ++h)
+                acc[h][nb] = mfma16_bf16(as_bf16x8(a[h]), as_bf16x8(bv), acc[h][nb]);
+            }
           }
         }
         // advance the queue
@@ -547,7 +612,7 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(4))) void
 // Within a chunk, the next batch of source chunks loads while the current one
 // is mixed.
 // ---------------------------------------------------------------------------
-template <int B, int D>
+template <int B, int D, int FMT>
 struct ApplyMixCfg {
   static constexpr int G = (4 * D * B * 2 <= 64 * 1024) ? 4 : 2;  // targets per work-group
   static constexpr int NW = B / 16;                 // waves, 16 rows each
@@ -556,6 +621,8 @@ struct ApplyMixCfg {
   static constexpr int VBYTES = D * B * 2;
   static constexpr int VINST = VBYTES / 1024 / NW;  // 1 KB direct loads per wave per V tile
   static constexpr int SB = 4;                      // sources per load batch (two pairs)
+  static constexpr int NP = (FMT == MF_TILE_MXFP8 && B >= 64) ? 2 : 1;  // fp8 chunks per piece
+  static constexpr int64_t TBYTES = tile_bytes(B, FMT);
   static_assert(VINST * 1024 * NW == VBYTES, "V tile must split into 1 KB wave loads");
   static_assert(G * VBYTES <= 64 * 1024, "V buffers must stay in the first 64 KB of LDS");
 };
@@ -574,16 +641,17 @@ inline size_t mix_smem(int B, int Hs, int nbw) {
   return s;
 }
 
-template <int B, int D>
+template <int B, int D, int FMT>
 __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(2))) void k_apply_mix(
     const int64_t *__restrict__ row_ptr, const int32_t *__restrict__ col_idx,
-    const uint16_t *__restrict__ tiles, const float *__restrict__ kept_mass, int32_t Hs,
+    const char *__restrict__ tiles, const float *__restrict__ kept_mass, int32_t Hs,
     int32_t NBR, int64_t T, const float *__restrict__ W, int32_t Ht, int32_t grp,
     const uint16_t *__restrict__ vt, const RowInfo *__restrict__ rows,
     const int32_t *__restrict__ sched, int32_t nbw, int64_t capacity, int32_t renorm,
     float *__restrict__ o, const int32_t *__restrict__ row_alias) {
-  using C = ApplyMixCfg<B, D>;
-  constexpr int G = C::G, KC = C::KC, SB = C::SB;
+  using C = ApplyMixCfg<B, D, FMT>;
+  constexpr int G = C::G, KC = C::KC, SB = C::SB, NP = C::NP;
+  constexpr bool FP8 = FMT == MF_TILE_MXFP8;
   __shared__ __attribute__((aligned(16))) char vbuf[G * C::VBYTES];
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int o_src = 0;
@@ -731,7 +799,10 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(2))) void
     if (t0 + g < Ht) nvh = (t0 + g) / grp - gv0 + 1;
 
   const int r0 = wave * 16 + m16;                 // lane row inside the block
-  const int loff = (wave * KC * 64 + lane) * 8;   // lane's 16 bytes of chunk 0 (elements)
+  // lane's bytes of chunk kc: bf16 16 bytes at loff + kc * 1024; fp8 8 bytes at
+  // loff + (kc / NP) * 512 NP + (kc % NP) * 8, and its row's scale byte
+  const int loff = FP8 ? (wave * (KC / NP) * 64 + lane) * 8 * NP : (wave * KC * 64 + lane) * 16;
+  const int soff = B * B + r0 * (B / 32);
   f32x4 acc[G][D / 16];
 #pragma unroll
   for (int g = 0; g < G; ++g)
@@ -766,13 +837,23 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(2))) void
                                  col0, wave, lane);
 
     u32x4 amix[G];
-    auto load_batch = [&](u32x4 (&d)[SB], int kc, int u0) {
+    auto load_batch = [&](u32x4 (&d)[SB], uint32_t (&sb)[SB], int kc, int u0) {
 #pragma unroll
       for (int e = 0; e < SB; ++e) {
         const int t_ = tile_at(u0 + e);
         d[e] = u32x4{0u, 0u, 0u, 0u};
-        if (t_ >= 0)
-          d[e] = *reinterpret_cast<const u32x4 *>(tiles + (int64_t)t_ * (B * B) + loff + kc * 512);
+        sb[e] = 0u;
+        if (t_ >= 0) {
+          const char *tp = tiles + (int64_t)t_ * C::TBYTES;
+          if constexpr (!FP8) {
+            d[e] = *reinterpret_cast<const u32x4 *>(tp + loff + kc * 1024);
+          } else {
+            const u32x2 c2 =
+                *reinterpret_cast<const u32x2 *>(tp + loff + (kc / NP) * 512 * NP + (kc % NP) * 8);
+            d[e] = u32x4{c2[0], c2[1], 0u, 0u};
+            sb[e] = *reinterpret_cast<const uint8_t *>(tp + soff + kc);
+          }
+        }
       }
     };
 #pragma unroll
@@ -783,14 +864,20 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(2))) void
 #pragma unroll
         for (int e = 0; e < 8; ++e) mx[g][e] = 0.f;
       u32x4 cur[SB], nxt[SB];
-      load_batch(cur, kc, 0);
+      uint32_t scur[SB], snxt[SB];
+      load_batch(cur, scur, kc, 0);
       for (int u0 = 0; u0 < ns; u0 += SB) {
-        if (u0 + SB < ns) load_batch(nxt, kc, u0 + SB);
+        if (u0 + SB < ns) load_batch(nxt, snxt, kc, u0 + SB);
 #pragma unroll
         for (int pr = 0; pr < SB / 2; ++pr) {
           const int u1 = u0 + 2 * pr, u2 = u1 + 1;
-          const float ra = u1 < ns ? rtab[u1 * B + r0] : 0.f;
-          const float rb = u2 < ns ? rtab[u2 * B + r0] : 0.f;
+          float ra = u1 < ns ? rtab[u1 * B + r0] : 0.f;
+          float rb = u2 < ns ? rtab[u2 * B + r0] : 0.f;
+          if constexpr (FP8) {
+            // the block scales 2^(byte - 127) folded into the coefficients
+            ra = __builtin_amdgcn_ldexpf(ra, (int)scur[2 * pr] - 127);
+            rb = __builtin_amdgcn_ldexpf(rb, (int)scur[2 * pr + 1] - 127);
+          }
           uint32_t cp[G];
 #pragma unroll
           for (int g = 0; g < G; ++g) {
@@ -798,21 +885,46 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(2))) void
             const float wb = u2 < ns ? wtab[u2 * 4 + g] : 0.f;
             cp[g] = pack_bf16x2(wa * ra, wb * rb);
           }
+          if constexpr (!FP8) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t lo = __builtin_amdgcn_perm(cur[2 * pr + 1][e], cur[2 * pr][e], 0x05040100u);
-            const uint32_t hi = __builtin_amdgcn_perm(cur[2 * pr + 1][e], cur[2 * pr][e], 0x07060302u);
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t lo = __builtin_amdgcn_perm(cur[2 * pr + 1][e], cur[2 * pr][e], 0x05040100u);
+              const uint32_t hi = __builtin_amdgcn_perm(cur[2 * pr + 1][e], cur[2 * pr][e], 0x07060302u);
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-              mx[g][2 * e] = __builtin_amdgcn_fdot2_f32_bf16(
-                  __builtin_bit_cast(bf16x2, lo), __builtin_bit_cast(bf16x2, cp[g]), mx[g][2 * e], false);
-              mx[g][2 * e + 1] = __builtin_amdgcn_fdot2_f32_bf16(
-                  __builtin_bit_cast(bf16x2, hi), __builtin_bit_cast(bf16x2, cp[g]), mx[g][2 * e + 1], false);
+              for (int g = 0; g < G; ++g) {
+                mx[g][2 * e] = __builtin_amdgcn_fdot2_f32_bf16(
+                    __builtin_bit_cast(bf16x2, lo), __builtin_bit_cast(bf16x2, cp[g]), mx[g][2 * e], false);
+                mx[g][2 * e + 1] = __builtin_amdgcn_fdot2_f32_bf16(
+                    __builtin_bit_cast(bf16x2, hi), __builtin_bit_cast(bf16x2, cp[g]), mx[g][2 * e + 1], false);
+              }
             }
+          } else {
+            // byte pairs [P1[e], P2[e]] of the two sources' codes, then E4M3 ->
+            // bf16 (exact: 3 mantissa bits, and the scale 1 changes nothing)
+#pragma unroll
+            for (int w = 0; w < 2; ++w)
+#pragma unroll
+              for (int hw = 0; hw < 2; ++hw) {
+                const uint32_t pairs = __builtin_amdgcn_perm(
+                    cur[2 * pr + 1][w], cur[2 * pr][w], hw ? 0x07030602u : 0x05010400u);
+                const bf16x2 pv[2] = {__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(pairs, 1.0f, false),
+                                      __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(pairs, 1.0f, true)};
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                  const int e = 4 * w + 2 * hw + k;
+#pragma unroll
+                  for (int g = 0; g < G; ++g)
+                    mx[g][e] = __builtin_amdgcn_fdot2_f32_bf16(pv[k], __builtin_bit_cast(bf16x2, cp[g]),
+                                                               mx[g][e], false);
+                }
+              }
           }
         }
 #pragma unroll
-        for (int e = 0; e < SB; ++e) cur[e] = nxt[e];
+        for (int e = 0; e < SB; ++e) {
+          cur[e] = nxt[e];
+          scur[e] = snxt[e];
+        }
       }
 #pragma unroll
       for (int g = 0; g < G; ++g)
@@ -854,6 +966,41 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(2))) void
   }
 }
 
+// The two apply kernels for one tile format.
+template <int B, int D, int FMT>
+static mf_status launch_apply_fmt(hipStream_t s, const mf_bsr_map *map, const float *W, int32_t Ht,
+                                  int32_t Hkv, const SeqGeom &g, int32_t renorm, float *o,
+                                  void *ws, const VtWs &w, int nbw, size_t smem, size_t smem_mix,
+                                  size_t vbufs, size_t vbufs_mix) {
+  using CM = ApplyMixCfg<B, D, FMT>;
+  if (smem + vbufs > 64 * 1024 &&
+      hipFuncSetAttribute(reinterpret_cast<const void *>(&k_apply4<B, D, FMT>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
+    return MF_ERR_HIP;
+  if (smem_mix + vbufs_mix > 64 * 1024 &&
+      hipFuncSetAttribute(reinterpret_cast<const void *>(&k_apply_mix<B, D, FMT>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem_mix) != hipSuccess)
+    return MF_ERR_HIP;
+  const char *tiles = static_cast<const char *>(map->tiles);
+  const int64_t npos = ((int64_t)g.NBR + kXcds - 1) / kXcds * kXcds;
+  // one launch per source-count class; a work-group whose targets are all of
+  // the other class returns right after reading their weight rows
+  hipLaunchKernelGGL((k_apply4<B, D, FMT>), dim3((unsigned)(npos * Ht)),
+                     dim3(Apply4Cfg<B, D, FMT>::NT), smem, s, map->row_ptr, map->col_idx, tiles,
+                     map->kept_mass, map->num_heads, g.NBR, g.T, W, Ht, Ht / Hkv,
+                     at<uint16_t>(ws, w.vt), at<RowInfo>(ws, w.rt.rows),
+                     at<int32_t>(ws, w.rt.sched), nbw, map->capacity_tiles, renorm, o,
+                     map->row_alias);
+  if (hip_status() != MF_OK) return MF_ERR_HIP;
+  const int64_t ngrp = (Ht + CM::G - 1) / CM::G;
+  hipLaunchKernelGGL((k_apply_mix<B, D, FMT>), dim3((unsigned)(npos * ngrp)), dim3(CM::NT),
+                     smem_mix, s, map->row_ptr, map->col_idx, tiles, map->kept_mass,
+                     map->num_heads, g.NBR, g.T, W, Ht, Ht / Hkv, at<uint16_t>(ws, w.vt),
+                     at<RowInfo>(ws, w.rt.rows), at<int32_t>(ws, w.rt.sched), nbw,
+                     map->capacity_tiles, renorm, o, map->row_alias);
+  return hip_status();
+}
+
 template <int B, int D>
 static mf_status launch_apply(hipStream_t s, const mf_bsr_map *map, const float *W, int32_t Ht,
                               const void *v, int32_t Hkv, const SeqGeom &g, int32_t renorm,
@@ -867,37 +1014,17 @@ static mf_status launch_apply(hipStream_t s, const mf_bsr_map *map, const float 
   if ((int64_t)D * g.NBR * B * 2 >= ((int64_t)1 << 31)) return MF_ERR_UNSUPPORTED;
   if (map->num_heads > kMixMaxSources) return MF_ERR_UNSUPPORTED;
   const size_t vbufs = 2 * (size_t)B * D * 2;  // the two static V tile buffers of k_apply4
-  const size_t vbufs_mix = (size_t)ApplyMixCfg<B, D>::G * B * D * 2;
+  const size_t vbufs_mix = (size_t)ApplyMixCfg<B, D, MF_TILE_BF16>::G * B * D * 2;
   if (smem + vbufs > 160 * 1024 || smem_mix + vbufs_mix > 160 * 1024) return MF_ERR_UNSUPPORTED;
   hipLaunchKernelGGL((k_vtranspose<B, D>), dim3(g.NBR, Hkv), dim3(256), 0, s,
                      reinterpret_cast<const uint16_t *>(v), g.T, at<RowInfo>(ws, w.rt.rows), g.NBR,
                      at<uint16_t>(ws, w.vt));
   if (hip_status() != MF_OK) return MF_ERR_HIP;
-  if (smem + vbufs > 64 * 1024 &&
-      hipFuncSetAttribute(reinterpret_cast<const void *>(&k_apply4<B, D>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
-    return MF_ERR_HIP;
-  if (smem_mix + vbufs_mix > 64 * 1024 &&
-      hipFuncSetAttribute(reinterpret_cast<const void *>(&k_apply_mix<B, D>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem_mix) != hipSuccess)
-    return MF_ERR_HIP;
-  const int64_t npos = ((int64_t)g.NBR + kXcds - 1) / kXcds * kXcds;
-  // one launch per source-count class; a work-group whose targets are all of
-  // the other class returns right after reading their weight rows
-  hipLaunchKernelGGL((k_apply4<B, D>), dim3((unsigned)(npos * Ht)), dim3(Apply4Cfg<B, D>::NT),
-                     smem, s, map->row_ptr, map->col_idx, map->tiles, map->kept_mass,
-                     map->num_heads, g.NBR, g.T, W, Ht, Ht / Hkv, at<uint16_t>(ws, w.vt),
-                     at<RowInfo>(ws, w.rt.rows), at<int32_t>(ws, w.rt.sched), nbw,
-                     map->capacity_tiles, renorm, o, map->row_alias);
-  if (hip_status() != MF_OK) return MF_ERR_HIP;
-  const int64_t ngrp = (Ht + ApplyMixCfg<B, D>::G - 1) / ApplyMixCfg<B, D>::G;
-  hipLaunchKernelGGL((k_apply_mix<B, D>), dim3((unsigned)(npos * ngrp)),
-                     dim3(ApplyMixCfg<B, D>::NT), smem_mix, s, map->row_ptr, map->col_idx,
-                     map->tiles, map->kept_mass, map->num_heads, g.NBR, g.T, W, Ht, Ht / Hkv,
-                     at<uint16_t>(ws, w.vt), at<RowInfo>(ws, w.rt.rows),
-                     at<int32_t>(ws, w.rt.sched), nbw, map->capacity_tiles, renorm, o,
-                     map->row_alias);
-  return hip_status();
+  if (map->tile_format == MF_TILE_MXFP8)
+    return launch_apply_fmt<B, D, MF_TILE_MXFP8>(s, map, W, Ht, Hkv, g, renorm, o, ws, w, nbw,
+                                                 smem, smem_mix, vbufs, vbufs_mix);
+  return launch_apply_fmt<B, D, MF_TILE_BF16>(s, map, W, Ht, Hkv, g, renorm, o, ws, w, nbw, smem,
+                                              smem_mix, vbufs, vbufs_mix);
 }
 
 }  // namespace mf
@@ -920,7 +1047,7 @@ extern "C" mf_status mf_apply_translated(void *stream, const mf_bsr_map *map, co
     return MF_ERR_INVALID_ARG;
   if (!valid_block(map->block)) return MF_ERR_INVALID_ARG;
   if (!valid_dim(d)) return MF_ERR_UNSUPPORTED;
-  if (map->num_heads <= 0 || !W) return MF_ERR_INVALID_ARG;
+  if (map->num_heads <= 0 || !W || !valid_tile_format(map->tile_format)) return MF_ERR_INVALID_ARG;
   SeqGeom g;
   mf_status st = seq_geom(cu_host, nseq, map->block, &g);
   if (st != MF_OK) return st;

@@ -14,9 +14,10 @@
 //              normaliser and mass passes.
 //   k_offsets  exclusive scan of kept counts -> row_ptr, nnz, capacity status.
 //   k_tiles    one work-group per (source head, query block): recomputes only
-//              the kept tiles, rounds exp2(x - lse2) to bf16 (nearest even),
-//              reorders them through LDS into fragment order (see mf_bsr_map)
-//              and writes each tile with coalesced 16-byte stores, plus col_idx.
+//              the kept tiles, rounds exp2(x - lse2) to bf16 (nearest even) or
+//              encodes it as block-scaled E4M3, exchanges lane halves with
+//              v_permlane32_swap into fragment order (see mf_bsr_map) and
+//              writes each tile with coalesced 16-byte stores, plus col_idx.
 #include <type_traits>
 
 #include "mf_host.hpp"
@@ -320,13 +321,74 @@ __device__ __forceinline__ void store_tile_rows(char *dst, const uint2 (&w)[B / 
     }
 }
 
-template <int B, int D, bool F32>
+// Block-scaled E4M3 form of one wave's 32 rows of a kept tile (format in
+// mf_bsr_map).  Per 32-key block of row m, the lane's 16 probabilities and its
+// partner's (lane ^ 32) give the block maximum a; its scale exponent is
+// e = max(floor(log2 a) - 7, -126), read off the fp32 exponent field (0 for
+// a = 0 or a denormal a, giving -126).  p * 2^-e is exact (a power-of-two
+// scale, at most 2^126) and below 256, and v_cvt_pk_fp8_f32 rounds it to the
+// nearest-even E4M3 code.  After the same v_permlane32_swap as the bf16 path,
+// lanes 0-31 hold 8-key run 2p and lanes 32-63 run 2p + 1 of both chunks of a
+// 64-key piece (one chunk for B = 32), which is one 16-byte (8-byte) piece.
+template <int B>
+__device__ __forceinline__ void store_tile_fp8(char *dst, const f32x16 (&pv)[B / 32], int wave,
+                                               int lane) {
+  constexpr int NP = B >= 64 ? 2 : 1;
+  const int m = lane & 31, hl = lane >> 5;
+  const int i_loc = wave * 32 + m;
+  uint32_t d[B / 32][4];
+  uint32_t sbytes = 0u;
+#pragma unroll
+  for (int mb = 0; mb < B / 32; ++mb) {
+    float a = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) a = max3(a, pv[mb][r], pv[mb][r + 1]);
+    a = pair_max(a);
+    const int E = (int)(__float_as_uint(a) >> 23) - 127;
+    const int e = E - 7 > -126 ? E - 7 : -126;
+    const float up = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e
+    sbytes |= (uint32_t)(e + 127) << (8 * mb);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(pv[mb][4 * g + 0] * up, pv[mb][4 * g + 1] * up, 0u, false);
+      d[mb][g] = __builtin_amdgcn_cvt_pk_fp8_f32(pv[mb][4 * g + 2] * up, pv[mb][4 * g + 3] * up, w, true);
+    }
+  }
+#pragma unroll
+  for (int cp = 0; cp < B / 32 / NP; ++cp)
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr) {
+      const int q = 2 * pr + hl;
+      const int piece = (i_loc >> 4) * (B / 32 / NP) + cp;
+      const auto s0 = __builtin_amdgcn_permlane32_swap(d[NP * cp][2 * pr], d[NP * cp][2 * pr + 1], false, false);
+      if constexpr (NP == 2) {
+        const auto s1 = __builtin_amdgcn_permlane32_swap(d[2 * cp + 1][2 * pr], d[2 * cp + 1][2 * pr + 1], false, false);
+        const u32x4 chunk = u32x4{s0[0], s0[1], s1[0], s1[1]};
+        __builtin_nontemporal_store(chunk, reinterpret_cast<u32x4 *>(dst + (piece * 64 + q * 16 + (i_loc & 15)) * 16));
+      } else {
+        const u32x2 chunk = u32x2{s0[0], s0[1]};
+        __builtin_nontemporal_store(chunk, reinterpret_cast<u32x2 *>(dst + (piece * 64 + q * 16 + (i_loc & 15)) * 8));
+      }
+    }
+  // scale bytes of row i_loc, written by the lower lane half
+  char *sdst = dst + B * B + i_loc * (B / 32);
+  if (hl == 0) {
+    if constexpr (B == 128)
+      __builtin_nontemporal_store(sbytes, reinterpret_cast<uint32_t *>(sdst));
+    else if constexpr (B == 64)
+      __builtin_nontemporal_store((uint16_t)sbytes, reinterpret_cast<uint16_t *>(sdst));
+    else
+      __builtin_nontemporal_store((uint8_t)sbytes, reinterpret_cast<uint8_t *>(sdst));
+  }
+}
+
+template <int B, int D, bool F32, int FMT>
 __global__ __launch_bounds__(B * 2) __attribute__((amdgpu_waves_per_eu(F32 ? 1 : 2))) void k_tiles(
     const void *__restrict__ qv, const void *__restrict__ kv, int64_t T, int32_t Hs, int32_t NBR,
     const RowInfo *__restrict__ rows, const int32_t *__restrict__ sched, float scale2,
     BiasArgs bias, const float *__restrict__ lse2_in, const uint32_t *__restrict__ bitmaps,
     int32_t nbw, const int64_t *__restrict__ row_ptr, int64_t capacity,
-    int32_t *__restrict__ col_idx, uint16_t *__restrict__ tiles) {
+    int32_t *__restrict__ col_idx, char *__restrict__ tiles) {
   using C = QKCfg<B, D, F32>;
   using TC = TilesCfg<B, D, F32>;
   using E = std::conditional_t<F32, float, uint16_t>;
@@ -400,30 +462,37 @@ __global__ __launch_bounds__(B * 2) __attribute__((amdgpu_waves_per_eu(F32 ? 1 :
     }
     f32x16 acc[B / 32];
     st_tile<B, D>(acc, kcur, qo, lane);
-    uint2 w[B / 32][4];
+    // probabilities, in place
     float off;
     if (uniform_tile(I, J, B, bias.sink_n, bias.sink2, bias.local_w, bias.local2, off)) {
       const float c0 = nlse2 + off;
 #pragma unroll
       for (int mb = 0; mb < B / 32; ++mb)
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-          w[mb][g] = pack4(fast_exp2(fmaf(acc[mb][4 * g + 0], scale2, c0)),
-                           fast_exp2(fmaf(acc[mb][4 * g + 1], scale2, c0)),
-                           fast_exp2(fmaf(acc[mb][4 * g + 2], scale2, c0)),
-                           fast_exp2(fmaf(acc[mb][4 * g + 3], scale2, c0)));
+        for (int r = 0; r < 16; ++r) acc[mb][r] = fast_exp2(fmaf(acc[mb][r], scale2, c0));
     } else {
       logits_inplace<B>(acc, false, rvalid, i_pos, J * B, scale2, bias.sink_n, bias.sink2,
                         bias.local_w, bias.local2, lane);
 #pragma unroll
       for (int mb = 0; mb < B / 32; ++mb)
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-          w[mb][g] = pack4(fast_exp2(acc[mb][4 * g + 0] + nlse2), fast_exp2(acc[mb][4 * g + 1] + nlse2),
-                           fast_exp2(acc[mb][4 * g + 2] + nlse2), fast_exp2(acc[mb][4 * g + 3] + nlse2));
+        for (int r = 0; r < 16; ++r) acc[mb][r] = fast_exp2(acc[mb][r] + nlse2);
     }
-    if (base + c < capacity)
-      store_tile_rows<B>(reinterpret_cast<char *>(tiles + (base + c) * (int64_t)B * B), w, wave, lane);
+    if (base + c < capacity) {
+      char *dst = tiles + (base + c) * tile_bytes(B, FMT);
+      if constexpr (FMT == MF_TILE_MXFP8) {
+        store_tile_fp8<B>(dst, acc, wave, lane);
+      } else {
+        uint2 w[B / 32][4];
+#pragma unroll
+        for (int mb = 0; mb < B / 32; ++mb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            w[mb][g] = pack4(acc[mb][4 * g + 0], acc[mb][4 * g + 1], acc[mb][4 * g + 2],
+                             acc[mb][4 * g + 3]);
+        store_tile_rows<B>(dst, w, wave, lane);
+      }
+    }
     // the other buffer held tile c - 1, whose readers all passed the last barrier
     if (c + 1 < cnt) lstore_tile<B, D, F32>(knext, stg, tid);
     __syncthreads();
@@ -455,10 +524,17 @@ static mf_status launch_compress(hipStream_t s, const void *q, const void *k, co
                      (int64_t)Hs * g.NBR, map->capacity_tiles, map->row_ptr, map->nnz,
                      map->status);
   if (hip_status() != MF_OK) return MF_ERR_HIP;
-  hipLaunchKernelGGL((k_tiles<B, D, F32>), grid, dim3(B * 2), 0, s, q, k, g.T, Hs, g.NBR,
-                     at<RowInfo>(ws, w.rt.rows), at<int32_t>(ws, w.rt.sched), scale2, ba,
-                     at<float>(ws, w.lse2), at<uint32_t>(ws, w.bitmaps), w.nbw, map->row_ptr,
-                     map->capacity_tiles, map->col_idx, map->tiles);
+  char *tiles = static_cast<char *>(map->tiles);
+  if (map->tile_format == MF_TILE_MXFP8)
+    hipLaunchKernelGGL((k_tiles<B, D, F32, MF_TILE_MXFP8>), grid, dim3(B * 2), 0, s, q, k, g.T,
+                       Hs, g.NBR, at<RowInfo>(ws, w.rt.rows), at<int32_t>(ws, w.rt.sched),
+                       scale2, ba, at<float>(ws, w.lse2), at<uint32_t>(ws, w.bitmaps), w.nbw,
+                       map->row_ptr, map->capacity_tiles, map->col_idx, tiles);
+  else
+    hipLaunchKernelGGL((k_tiles<B, D, F32, MF_TILE_BF16>), grid, dim3(B * 2), 0, s, q, k, g.T,
+                       Hs, g.NBR, at<RowInfo>(ws, w.rt.rows), at<int32_t>(ws, w.rt.sched),
+                       scale2, ba, at<float>(ws, w.lse2), at<uint32_t>(ws, w.bitmaps), w.nbw,
+                       map->row_ptr, map->capacity_tiles, map->col_idx, tiles);
   return hip_status();
 }
 
@@ -481,6 +557,11 @@ extern "C" int32_t mf_num_block_rows(const int32_t *cu, int32_t nseq, int32_t B)
   SeqGeom g;
   if (seq_geom(cu, nseq, B, &g) != MF_OK) return -1;
   return g.NBR;
+}
+
+extern "C" int64_t mf_tile_bytes(int32_t B, int32_t tile_format) {
+  if (!valid_block(B) || !valid_tile_format(tile_format)) return 0;
+  return tile_bytes(B, tile_format);
 }
 
 extern "C" int64_t mf_compress_max_tiles(int32_t Hs, const int32_t *cu, int32_t nseq, int32_t B) {
@@ -512,6 +593,7 @@ extern "C" mf_status mf_compress_topp(void *stream, const void *q, const void *k
   if (map->capacity_tiles < 0 || !map->row_ptr || !map->nnz || !map->status) return MF_ERR_INVALID_ARG;
   if (g.T > 0 && (!q || !k || !map->kept_mass)) return MF_ERR_INVALID_ARG;
   if (map->capacity_tiles > 0 && (!map->col_idx || !map->tiles)) return MF_ERR_INVALID_ARG;
+  if (!valid_tile_format(map->tile_format)) return MF_ERR_INVALID_ARG;
   const CompressWs w = compress_ws(g, Hs, B);
   if (!ws || ws_bytes < w.total) return MF_ERR_WORKSPACE;
   void *wsa = reinterpret_cast<void *>((reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255));

@@ -20,6 +20,13 @@ struct SeqGeom {
 
 inline bool valid_block(int32_t B) { return B == 32 || B == 64 || B == 128; }
 inline bool valid_dim(int32_t d) { return d == 64 || d == 128; }
+inline bool valid_tile_format(int32_t f) { return f == MF_TILE_BF16 || f == MF_TILE_MXFP8; }
+
+// Bytes of one stored tile (codes, then one scale byte per 32 keys of a row, for
+// the block-scaled fp8 format).
+constexpr int64_t tile_bytes(int B, int fmt) {
+  return fmt == MF_TILE_MXFP8 ? (int64_t)B * B + (int64_t)B * (B / 32) : (int64_t)B * B * 2;
+}
 
 // Validates host offsets and fills the geometry. MF_ERR_UNSUPPORTED for too many
 // key blocks in one sequence.

@@ -19,11 +19,14 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmapflow.
 
 MF_OK, MF_ERR_INVALID_ARG, MF_ERR_UNSUPPORTED, MF_ERR_CAPACITY, MF_ERR_HIP, MF_ERR_WORKSPACE = range(6)
 MF_BF16, MF_FP32 = 0, 1
+MF_TILE_BF16, MF_TILE_MXFP8 = 0, 1
+TILE_FORMATS = {"bf16": MF_TILE_BF16, "mxfp8": MF_TILE_MXFP8}
 
 EXPORTS = ("mf_num_block_rows", "mf_compress_max_tiles", "mf_compress_workspace_bytes",
            "mf_compress_topp", "mf_apply_workspace_bytes", "mf_apply_translated",
            "mf_dense_workspace_bytes", "mf_dense_ref_attention", "mf_read_status",
-           "mf_status_string", "mf_prefix_dedupe_workspace_bytes", "mf_prefix_dedupe")
+           "mf_status_string", "mf_prefix_dedupe_workspace_bytes", "mf_prefix_dedupe",
+           "mf_tile_bytes")
 
 
 class MfLogitBias(ctypes.Structure):
@@ -37,7 +40,8 @@ class MfBsrMap(ctypes.Structure):
                 ("capacity_tiles", ctypes.c_int64), ("row_ptr", ctypes.c_void_p),
                 ("col_idx", ctypes.c_void_p), ("tiles", ctypes.c_void_p),
                 ("kept_mass", ctypes.c_void_p), ("nnz", ctypes.c_void_p),
-                ("status", ctypes.c_void_p), ("row_alias", ctypes.c_void_p)]
+                ("status", ctypes.c_void_p), ("row_alias", ctypes.c_void_p),
+                ("tile_format", ctypes.c_int32)]
 
 
 class MapflowError(RuntimeError):
@@ -75,6 +79,7 @@ def load():
         "mf_status_string": (ctypes.c_char_p, [i32]),
         "mf_prefix_dedupe_workspace_bytes": (sz, [pcu, i32, i32]),
         "mf_prefix_dedupe": (i32, [vp, vp, vp, i32, pcu, vp, i32, i32, i32, i32, vp, vp, sz]),
+        "mf_tile_bytes": (i64, [i32, i32]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -164,11 +169,12 @@ class BsrMap:
     total_tokens: int
     row_ptr: torch.Tensor      # int64 [Hs * NBR + 1]
     col_idx: torch.Tensor      # int32 [capacity]
-    tiles: torch.Tensor        # bfloat16 [capacity, B, B]
+    tiles: torch.Tensor        # bfloat16 [capacity, B, B], or uint8 [capacity, B*B + B*B/32] (mxfp8)
     kept_mass: torch.Tensor    # float32 [Hs, T]
     nnz: torch.Tensor          # int64 [1]
     status: torch.Tensor       # int32 [1]
     row_alias: Optional[torch.Tensor] = None  # int32 [NBR] from mf_prefix_dedupe, or None
+    tile_format: str = "bf16"  # "bf16" or "mxfp8"
 
     @property
     def capacity(self) -> int:
@@ -179,10 +185,18 @@ class BsrMap:
                         self.capacity, self.row_ptr.data_ptr(), self.col_idx.data_ptr(),
                         self.tiles.data_ptr(), self.kept_mass.data_ptr(), self.nnz.data_ptr(),
                         self.status.data_ptr(),
-                        self.row_alias.data_ptr() if self.row_alias is not None else None)
+                        self.row_alias.data_ptr() if self.row_alias is not None else None,
+                        TILE_FORMATS[self.tile_format])
 
 
-def alloc_map(Hs: int, cu_seqlens, B: int, device, capacity: Optional[int] = None) -> BsrMap:
+def mf_tile_bytes(B: int, tile_format: str = "bf16") -> int:
+    return int(load().mf_tile_bytes(B, TILE_FORMATS[tile_format]))
+
+
+def alloc_map(Hs: int, cu_seqlens, B: int, device, capacity: Optional[int] = None,
+              tile_format: str = "bf16") -> BsrMap:
+    if tile_format not in TILE_FORMATS:
+        raise ValueError(f"tile_format must be one of {sorted(TILE_FORMATS)}")
     cu = _cu_host(cu_seqlens)
     nbr = mf_num_block_rows(cu, B)
     if nbr < 0:
@@ -193,10 +207,14 @@ def alloc_map(Hs: int, cu_seqlens, B: int, device, capacity: Optional[int] = Non
     return BsrMap(Hs, B, nbr, T,
                   torch.zeros(Hs * nbr + 1, dtype=torch.int64, device=device),
                   torch.zeros(max(capacity, 0), dtype=torch.int32, device=device),
-                  torch.empty((max(capacity, 0), B, B), dtype=torch.bfloat16, device=device),
+                  (torch.empty((max(capacity, 0), B, B), dtype=torch.bfloat16, device=device)
+                   if tile_format == "bf16" else
+                   torch.empty((max(capacity, 0), mf_tile_bytes(B, tile_format)), dtype=torch.uint8,
+                               device=device)),
                   torch.zeros((Hs, T), dtype=torch.float32, device=device),
                   torch.zeros(1, dtype=torch.int64, device=device),
-                  torch.zeros(1, dtype=torch.int32, device=device))
+                  torch.zeros(1, dtype=torch.int32, device=device),
+                  tile_format=tile_format)
 
 
 def mf_prefix_dedupe_workspace_bytes(cu_seqlens, B: int) -> int:
@@ -235,10 +253,13 @@ def mf_compress_topp(q: torch.Tensor, k: torch.Tensor, cu_seqlens, B: int, p: fl
                      bias: Optional[dict] = None, out: Optional[BsrMap] = None,
                      capacity: Optional[int] = None, workspace: Optional[torch.Tensor] = None,
                      cu_dev: Optional[torch.Tensor] = None,
-                     row_alias: Optional[torch.Tensor] = None) -> BsrMap:
+                     row_alias: Optional[torch.Tensor] = None,
+                     tile_format: str = "bf16") -> BsrMap:
     """Block top-p compression of the causal maps of all heads of q, k ([Hs, T, d]).
     With row_alias (from mf_prefix_dedupe), block-rows that share an earlier one
-    are not computed; the map keeps the alias for retrieval."""
+    are not computed; the map keeps the alias for retrieval.  tile_format
+    "mxfp8" stores block-scaled E4M3 tiles (ignored when `out` is given: the
+    map's own format is used)."""
     lib = load()
     cu = _cu_host(cu_seqlens)
     Hs, T, d = q.shape
@@ -247,7 +268,7 @@ def mf_compress_topp(q: torch.Tensor, k: torch.Tensor, cu_seqlens, B: int, p: fl
     if not (q.is_contiguous() and k.is_contiguous()):
         raise ValueError("q and k must be contiguous")
     dev = q.device
-    m = out if out is not None else alloc_map(Hs, cu, B, dev, capacity)
+    m = out if out is not None else alloc_map(Hs, cu, B, dev, capacity, tile_format)
     if row_alias is not None and (row_alias.dtype != torch.int32 or not row_alias.is_contiguous()):
         raise ValueError("row_alias must be contiguous int32")
     m.row_alias = row_alias

@@ -77,6 +77,11 @@ typedef enum mf_status {
 
 typedef enum mf_dtype { MF_BF16 = 0, MF_FP32 = 1 } mf_dtype;
 
+/* How a compressed map stores its probability tiles (see mf_bsr_map).
+ * MF_TILE_MXFP8 is the quantised sparse map MapFlow §9 points to: E4M3 codes
+ * with one power-of-two scale per 32 keys of a row, half the bytes of bf16. */
+typedef enum mf_tile_format { MF_TILE_BF16 = 0, MF_TILE_MXFP8 = 1 } mf_tile_format;
+
 /* Logit offsets added after scaling: +sink_bias on key positions [0, sink_n) of
  * each sequence, +local_bias where 0 <= i - j < local_w.  Both may apply.  A
  * NULL pointer means no offsets. */
@@ -107,6 +112,24 @@ typedef struct mf_logit_bias {
  * kept_mass[h][token] is the sum, over the kept blocks of the token's row, of
  * its unrounded probabilities.
  *
+ * MF_TILE_MXFP8 tiles (mf_tile_bytes(B, MF_TILE_MXFP8) = B*B + B*B/32 bytes):
+ * every row of a tile is cut into B/32 blocks of 32 consecutive keys.  Block g
+ * of row i has the scale exponent e = max(floor(log2 a) - 7, -126), a being the
+ * block's largest fp32 probability (e = -126 for an all-zero block), stored as
+ * the byte e + 127; each element is the OCP E4M3 code (bias 7, no infinities)
+ * of p * 2^-e rounded to nearest even, so the block maximum scales into
+ * [128, 256) and nothing saturates.  A reader decodes code_value * 2^e; the
+ * error is at most max(2^-4 p, 2^(e-10)).  The first B*B bytes hold the codes:
+ * with NP = 2 for B >= 64 (1 for B = 32), the tile is cut into pieces of 16
+ * rows x 32*NP keys, piece (i/16, j/(32 NP)) being the
+ * ((i/16) * B/(32 NP) + j/(32 NP))-th block of 512*NP bytes; inside it, lane
+ * f = ((j%32)/8)*16 + i%16 holds 8*NP bytes: keys 8 of each 32-key chunk of
+ * the piece, chunk by chunk.  Element (i, j) is at
+ *   ((i/16 * B/(32 NP) + j/(32 NP)) * 64 + (j%32)/8 * 16 + i%16) * 8 NP
+ *     + ((j % (32 NP)) / 32) * 8 + j%8.
+ * The last B*B/32 bytes hold the scale bytes row by row: row i, block g at
+ * B*B + i * B/32 + g.
+ *
  * The caller allocates every array and sets the pointers and capacity_tiles;
  * mf_compress_topp fills the four size fields and the arrays.  Apply only reads
  * the map, so one map can serve any number of apply calls (MapFlow §5.2: one
@@ -126,16 +149,21 @@ typedef struct mf_bsr_map {
   int64_t capacity_tiles;  /* tiles/col_idx entries allocated            (in) */
   int64_t *row_ptr;        /* [Hs * NBR + 1]                                  */
   int32_t *col_idx;        /* [capacity_tiles]                                */
-  uint16_t *tiles;         /* [capacity_tiles][B][B] bf16 bit patterns        */
+  void *tiles;             /* [capacity_tiles] tiles of mf_tile_bytes(B, tile_format) bytes */
   float *kept_mass;        /* [Hs][T]                                         */
   int64_t *nnz;            /* device scalar: number of kept tiles             */
   int32_t *status;         /* device scalar: MF_OK or MF_ERR_CAPACITY         */
   const int32_t *row_alias; /* [NBR] or NULL: shared block-rows (see above)     */
+  int32_t tile_format;     /* mf_tile_format of the tiles                 (in) */
 } mf_bsr_map;
 
 /* Number of global block-rows sum_s ceil(L_s / B); -1 if the offsets are invalid.
  * cu_seqlens_host: host, nseq + 1 entries. */
 int32_t mf_num_block_rows(const int32_t *cu_seqlens_host, int32_t nseq, int32_t B);
+
+/* Bytes of one stored tile: B*B*2 for MF_TILE_BF16, B*B + B*B/32 for
+ * MF_TILE_MXFP8; 0 if B or the format is not supported. */
+int64_t mf_tile_bytes(int32_t B, int32_t tile_format);
 
 /* Worst-case kept tiles (every causal block): Hs * sum_s nb_s (nb_s + 1) / 2.
  * -1 if the arguments are invalid.  A smaller capacity is allowed; overflow is

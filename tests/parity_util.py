@@ -7,10 +7,17 @@ to the cut band; everything else to fixed tolerances):
               cut-ambiguous (mass within 1e-5 relative of the cut);
   tiles       |bf16 tile - P| <= 2e-3 on blocks kept by both (bf16 rounding of a
               probability <= 1 is at most 2^-9 ~ 1.95e-3 with nearest-even);
+  fp8 tiles   (block-scaled E4M3 maps) scale bytes and codes equal the oracle
+              codec's applied to the fp64 probabilities, except where the fp64
+              value sits within FP8_EPS (relative) of a decision boundary (a
+              power of two for a block maximum, a rounding midpoint for a code):
+              there the kernel's fp32 probability may fall on either side;
+              decoded values within the codec's bound max(2^-4 p, 2^(e-10));
   kept mass   1e-4 relative where the sets agree (fp32 sums of fp32 exponentials);
   outputs     relative Frobenius error <= 1e-2 per (sequence, target head), over
               the rows compared (bf16 tiles and bf16 mixed tiles feeding fp32
-              accumulation: per-element rounding 2^-9, averaged over a row).
+              accumulation: per-element rounding 2^-9, averaged over a row); for
+              fp8 maps against the oracle reading its own codec's tiles.
 """
 from __future__ import annotations
 
@@ -21,9 +28,11 @@ import numpy as np
 import torch
 
 from oracle import mapflow_oracle as orc
+from oracle import mx_codec as mx
 from cross_model_sparse_amd import mapflow as mf
 
 TILE_ATOL = 2e-3
+FP8_EPS = 3e-5      # relative distance of an fp64 value to an fp8 decision boundary
 KMASS_RTOL = 1e-4
 OUT_RFROB = 1e-2
 
@@ -47,10 +56,10 @@ def to_dev_v(wl, dev):
     return torch.from_numpy(wl.v_bits.view(np.int16)).to(dev).view(torch.bfloat16)
 
 
-def gpu_compress(wl, dev, p=None, capacity=None):
+def gpu_compress(wl, dev, p=None, capacity=None, tile_format="bf16"):
     q, k = to_dev_qk(wl, dev)
     m = mf.mf_compress_topp(q, k, wl.cu_seqlens, wl.spec.B, wl.spec.p if p is None else p,
-                            wl.bias(), capacity=capacity)
+                            wl.bias(), capacity=capacity, tile_format=tile_format)
     st, nnz = mf.mf_read_status(m)
     return m, st, nnz
 
@@ -66,18 +75,62 @@ def tiles_to_rowmajor(t: np.ndarray) -> np.ndarray:
     return flat[:, off]
 
 
+def fp8_tiles_unpack(raw: np.ndarray, B: int) -> Tuple[np.ndarray, np.ndarray]:
+    """[n, B*B + B*B/32] bytes as stored (layout in include/mapflow.h) ->
+    (codes [n, B, B] row-major, scale bytes [n, B, B/32])."""
+    n = raw.shape[0]
+    NP = 2 if B >= 64 else 1
+    i = np.arange(B)[:, None]
+    j = np.arange(B)[None, :]
+    off = ((((i // 16) * (B // (32 * NP)) + j // (32 * NP)) * 64 + ((j % 32) // 8) * 16 + i % 16) * 8 * NP
+           + ((j % (32 * NP)) // 32) * 8 + j % 8)
+    codes = raw[:, :B * B][:, off]
+    scales = raw[:, B * B:].reshape(n, B, B // 32)
+    return codes, scales
+
+
+def check_fp8_tile(codes: np.ndarray, scales: np.ndarray, P: np.ndarray, key) -> int:
+    """One fp8 tile against the oracle codec (module doc); returns the number of
+    codes that differ from the codec's at a rounding midpoint."""
+    B = P.shape[0]
+    G = B // 32
+    c_orc, s_orc = mx.encode_tile(P)
+    amax = P.reshape(B, G, 32).max(axis=2)
+    with np.errstate(divide="ignore"):
+        near_pow2 = (amax > 0) & (np.abs(amax / np.exp2(np.round(np.log2(np.where(amax > 0, amax, 1.0)))) - 1.0)
+                                  <= FP8_EPS)
+    bad = (scales != s_orc) & ~near_pow2
+    assert not bad.any(), f"tile {key}: scale bytes differ at {np.argwhere(bad)[:4].tolist()}"
+    e = scales.astype(np.int64) - mx.SCALE_BIAS
+    y = np.ldexp(P.reshape(B, G, 32), -e[:, :, None]).reshape(B, B)
+    assert y.max() < 448.0, f"tile {key}: a value does not fit the kernel's scale"
+    c_ref = mx.e4m3_codes(y)
+    mism = codes != c_ref
+    if mism.any():
+        vg, vr = mx.E4M3_TABLE[codes[mism]], mx.E4M3_TABLE[c_ref[mism]]
+        ym = y[mism]
+        ok = np.abs(vg - ym) - np.abs(vr - ym) <= 2 * FP8_EPS * ym
+        assert ok.all(), (f"tile {key}: codes {codes[mism][~ok][:4]} vs {c_ref[mism][~ok][:4]} "
+                          f"for scaled values {ym[~ok][:4]}")
+    dec = mx.decode_tile(codes, scales)
+    lim = mx.error_bound(P) * (1 + 2 * FP8_EPS) + 2 * FP8_EPS * P + 1e-30
+    assert np.all(np.abs(dec - P) <= lim), f"tile {key}: decoded value outside the codec bound"
+    return int(mism.sum())
+
+
 class HostMap:
     """CPU copy of the parts of a device map the checks need (selected rows only)."""
 
     def __init__(self, m: "mf.BsrMap", rows: Optional[Sequence[int]] = None):
         self.B = m.block
+        self.fmt = m.tile_format
         self.NBR = m.num_block_rows
         self.row_ptr = m.row_ptr.cpu().numpy()
         nnz = int(self.row_ptr[-1])
         self.kept_mass = m.kept_mass.cpu().numpy()
         if rows is None:
             self.col_idx = m.col_idx[:nnz].cpu().numpy()
-            self.tiles = tiles_to_rowmajor(m.tiles[:nnz].float().cpu().numpy())
+            self.tiles = self._host_tiles(m.tiles[:nnz])
             self.tile_base = 0
             self.rows = None
         else:
@@ -85,7 +138,7 @@ class HostMap:
             idx = np.concatenate([np.arange(self.row_ptr[r], self.row_ptr[r + 1]) for r in rows])
             it = torch.from_numpy(idx).to(m.col_idx.device)
             self.sel_col = m.col_idx[it].cpu().numpy()
-            self.sel_tiles = tiles_to_rowmajor(m.tiles[it].float().cpu().numpy())
+            self.sel_tiles = self._host_tiles(m.tiles[it])
             self.sel_pos = {}
             o = 0
             for r in rows:
@@ -93,6 +146,13 @@ class HostMap:
                 self.sel_pos[r] = (o, n)
                 o += n
             self.rows = set(rows)
+
+    def _host_tiles(self, t: torch.Tensor):
+        """bf16: row-major float tiles; fp8: (codes, scale bytes) row-major."""
+        if self.fmt == "bf16":
+            return tiles_to_rowmajor(t.float().cpu().numpy())
+        codes, scales = fp8_tiles_unpack(t.cpu().numpy(), self.B)
+        return list(zip(codes, scales))
 
     def row(self, r: int) -> Tuple[np.ndarray, np.ndarray]:
         """(col_idx, tiles) of BSR row r."""
@@ -111,7 +171,8 @@ def global_row(cu, B, s, I) -> int:
 def check_rows(hm: HostMap, res: Dict[Tuple[int, int, int], "orc.RowResult"], cu, T) -> dict:
     """Compare kept sets, tiles and kept mass of every oracle row in `res`."""
     B = hm.B
-    stats = dict(rows=0, ambiguous_rows=0, tile_err=0.0, kmass_err=0.0, flips=[])
+    stats = dict(rows=0, ambiguous_rows=0, tile_err=0.0, kmass_err=0.0, flips=[], fp8_mid=0,
+                 fp8_codes=0)
     for (h, s, I), rr in res.items():
         gr = global_row(cu, B, s, I)
         r = h * hm.NBR + gr
@@ -126,9 +187,17 @@ def check_rows(hm: HostMap, res: Dict[Tuple[int, int, int], "orc.RowResult"], cu
             stats["flips"].append((h, s, I))
         for c, J in enumerate(gset):
             if J in oset:
-                e = float(np.max(np.abs(tiles[c] - rr.tile(J, B))))
-                stats["tile_err"] = max(stats["tile_err"], e)
-                assert e <= TILE_ATOL, f"tile {(h, s, I, J)} max error {e}"
+                if hm.fmt == "bf16":
+                    e = float(np.max(np.abs(tiles[c] - rr.tile(J, B))))
+                    stats["tile_err"] = max(stats["tile_err"], e)
+                    assert e <= TILE_ATOL, f"tile {(h, s, I, J)} max error {e}"
+                else:
+                    codes, scales = tiles[c]
+                    P = rr.tile(J, B)
+                    stats["fp8_mid"] += check_fp8_tile(codes, scales, P, (h, s, I, J))
+                    stats["fp8_codes"] += codes.size
+                    e = float(np.max(np.abs(mx.decode_tile(codes, scales) - P)))
+                    stats["tile_err"] = max(stats["tile_err"], e)
         if not diff:
             a = int(cu[s]) + I * B
             km = hm.kept_mass[h, a:a + len(rr.rows)]

@@ -30,7 +30,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = header_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(mf.EXPORTS) == names
@@ -118,6 +118,27 @@ def test_prefix_dedupe_rejects_bad_arguments(lib):
     assert f(None, fake, fake, 0, pc, fake, 2, 4, 96, 32, fake, fake, need) == mf.MF_ERR_UNSUPPORTED
     assert f(None, fake, fake, 0, pc, fake, 2, 4, 64, 32, None, fake, need) == mf.MF_ERR_INVALID_ARG
     assert f(None, fake, fake, 0, pc, fake, 2, 4, 64, 32, fake, fake, need - 1) == mf.MF_ERR_WORKSPACE
+
+
+def test_tile_bytes(lib):
+    for B in (32, 64, 128):
+        assert lib.mf_tile_bytes(B, mf.MF_TILE_BF16) == B * B * 2
+        assert lib.mf_tile_bytes(B, mf.MF_TILE_MXFP8) == B * B + B * (B // 32)
+    assert lib.mf_tile_bytes(48, mf.MF_TILE_BF16) == 0
+    assert lib.mf_tile_bytes(64, 2) == 0
+    assert lib.mf_tile_bytes(64, -1) == 0
+
+
+def test_unknown_tile_format_rejected(lib):
+    c = cu([100])
+    fake = ctypes.c_void_p(16)
+    pc = c.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    m = mf.MfBsrMap(0, 0, 0, 0, 10, 8, 8, 8, 8, 8, 8, None, 2)
+    assert lib.mf_compress_topp(None, fake, fake, 0, pc, fake, 1, 2, 64, 32, 0.9, None,
+                                ctypes.byref(m), fake, 1 << 40) == mf.MF_ERR_INVALID_ARG
+    m = mf.MfBsrMap(2, 32, 4, 100, 10, 8, 8, 8, 8, 8, 8, None, 5)
+    assert lib.mf_apply_translated(None, ctypes.byref(m), fake, 4, fake, 2, 64, pc, fake, 1, 1,
+                                   fake, fake, 1 << 40) == mf.MF_ERR_INVALID_ARG
 
 
 def test_status_strings(lib):

@@ -19,13 +19,13 @@ from parity_util import (HostMap, check_apply, check_rows, gpu_compress, global_
 pytestmark = pytest.mark.gpu
 
 
-def full_case(wl, dev, p=None, W=None, renorm=True):
+def full_case(wl, dev, p=None, W=None, renorm=True, tile_format="bf16"):
     """Whole oracle vs whole HIP path on a small workload."""
     B = wl.spec.B
     p = wl.spec.p if p is None else p
     W = wl.W if W is None else W
-    say(f"case {wl.spec.name} lens={wl.lens[:8]} Hs={wl.spec.Hs} p={p} B={B}")
-    m, st, nnz = gpu_compress(wl, dev, p=p)
+    say(f"case {wl.spec.name} lens={wl.lens[:8]} Hs={wl.spec.Hs} p={p} B={B} tiles={tile_format}")
+    m, st, nnz = gpu_compress(wl, dev, p=p, tile_format=tile_format)
     assert st == mf.MF_OK
     res = orc.compress(wl.q, wl.k, wl.cu_seqlens, B, p, wl.bias())
     hm = HostMap(m)
@@ -36,11 +36,15 @@ def full_case(wl, dev, p=None, W=None, renorm=True):
         assert np.array_equal(hm.row_ptr, rp)
     Wt = torch.from_numpy(np.ascontiguousarray(W, dtype=np.float32)).to(dev)
     O = mf.mf_apply_translated(m, Wt, to_dev_v(wl, dev), wl.cu_seqlens, renorm=renorm)
-    out = orc.apply(res, W, wl.v, wl.cu_seqlens, B, wl.spec.Hkv, renorm=renorm)
+    codec = "mxfp8" if tile_format == "mxfp8" else None
+    out = orc.apply(res, W, wl.v, wl.cu_seqlens, B, wl.spec.Hkv, renorm=renorm, codec=codec)
     skip = {(s, I) for (h, s, I) in stats["flips"]}
     err = check_apply(O.cpu().numpy(), out, wl.cu_seqlens, B, skip)
     say(f"  rows={stats['rows']} flips={stats['ambiguous_rows']} tile_err={stats['tile_err']:.2e} "
-        f"kmass_err={stats['kmass_err']:.2e} out_err={err:.2e} nnz={nnz}")
+        f"kmass_err={stats['kmass_err']:.2e} out_err={err:.2e} nnz={nnz}"
+        + (f" fp8 midpoint codes {stats['fp8_mid']}/{stats['fp8_codes']}" if codec else ""))
+    if codec:
+        assert stats["fp8_mid"] <= 1e-3 * stats["fp8_codes"]
     return m, res, O, stats
 
 
@@ -342,6 +346,87 @@ def test_dedupe_full_size_multiturn(gpu):
             assert torch.equal(m0.col_idx[rp0[r0]:rp0[r0] + n], m1.col_idx[rp1[r1]:rp1[r1] + n])
             assert torch.equal(m0.tiles[rp0[r0]:rp0[r0] + n].view(torch.int16),
                                m1.tiles[rp1[r1]:rp1[r1] + n].view(torch.int16))
+    Wt, vd = torch.from_numpy(wl.W).to(gpu), to_dev_v(wl, gpu)
+    O0 = mf.mf_apply_translated(m0, Wt, vd, wl.cu_seqlens)
+    O1 = mf.mf_apply_translated(m1, Wt, vd, wl.cu_seqlens)
+    assert torch.equal(O0, O1)
+
+
+# ---------------------------------------------------------------------------
+# block-scaled fp8 tiles
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("idx,lens,kw", [
+    (2, [1000], dict(Hs=8, Ht=8, Hkv=8)),
+    (3, [777], dict(Hs=6, Ht=8, Hkv=2)),
+    (4, [1100], dict(Hs=8, Ht=16, Hkv=16)),
+    (5, [300, 520, 64, 1, 129, 0, 700], dict(Hs=4, Ht=4, Hkv=4)),
+])
+def test_fp8_small_variants(gpu, idx, lens, kw):
+    """fp8 maps: codes and scales against the oracle codec, outputs against the
+    oracle reading the codec's tiles; sparse (four sources) and dense W."""
+    full_case(wlmod.small_variant(idx, lens, **kw), gpu, tile_format="mxfp8")
+
+
+@pytest.mark.parametrize("B,d,dt", [(32, 128, "bf16"), (64, 64, "fp32"), (128, 128, "bf16")])
+def test_fp8_block_dim_grid(gpu, B, d, dt):
+    spec = wlmod.Spec(f"fp8 grid B={B} d={d} {dt}", (333, 200), 3, 4, 2, d, B, 0.85, dt, 48, "gauss",
+                      w_var=0.3, seed=200 + B + d)
+    full_case(wlmod.make_workload(spec), gpu, tile_format="mxfp8")
+
+
+@pytest.mark.parametrize("idx", [4, 5])
+def test_fp8_full_size_sampled(gpu, idx):
+    """Full-size workloads with fp8 maps at the benchmark's launch configuration:
+    sampled block-rows against the oracle codec; the fp8 map keeps the bf16 map's
+    structure (same row pointers and block indices) and half its tile bytes."""
+    wl = wlmod.make_config(idx)
+    B, Hs = wl.spec.B, wl.spec.Hs
+    rows = []
+    for (s, I) in SAMPLE_ROWS[idx]:
+        nb = (wl.lens[s] + B - 1) // B
+        rows.append((s, min(I, nb - 1)))
+    say(f"full workload {idx} fp8: T={wl.T} Hs={Hs} Ht={wl.spec.Ht} rows={rows}")
+    m, st, nnz = gpu_compress(wl, gpu, tile_format="mxfp8")
+    assert st == mf.MF_OK
+    mb, stb, nnzb = gpu_compress(wl, gpu)
+    assert stb == mf.MF_OK and nnzb == nnz
+    assert torch.equal(m.row_ptr, mb.row_ptr) and torch.equal(m.col_idx[:nnz], mb.col_idx[:nnz])
+    assert torch.equal(m.kept_mass, mb.kept_mass)
+    del mb
+    Wt = torch.from_numpy(wl.W).to(gpu)
+    vd = to_dev_v(wl, gpu)
+    O = mf.mf_apply_translated(m, Wt, vd, wl.cu_seqlens)
+    O2 = mf.mf_apply_translated(m, Wt, vd, wl.cu_seqlens)
+    assert torch.equal(O, O2), "fp8 retrieval is not deterministic at full size"
+    del O2
+    res = orc.compress(wl.q, wl.k, wl.cu_seqlens, B, wl.spec.p, wl.bias(), rows=rows)
+    brows = [h * m.num_block_rows + global_row(wl.cu_seqlens, B, s, I) for h in range(Hs) for (s, I) in rows]
+    hm = HostMap(m, rows=brows)
+    stats = check_rows(hm, res, wl.cu_seqlens, wl.T)
+    assert stats["fp8_mid"] <= 1e-3 * stats["fp8_codes"]
+    targets = [0, wl.spec.Ht // 3, wl.spec.Ht - 1]
+    out = orc.apply(res, wl.W, wl.v, wl.cu_seqlens, B, wl.spec.Hkv, targets=targets, rows=rows,
+                    codec="mxfp8")
+    Og = {t: O[t].cpu().numpy() for t in targets}
+    skip = {(s, I) for (h, s, I) in stats["flips"]}
+    err = check_apply(Og, out, wl.cu_seqlens, B, skip)
+    say(f"  nnz={nnz} rows={stats['rows']} flips={stats['ambiguous_rows']} tile_err={stats['tile_err']:.2e} "
+        f"out_err={err:.2e} fp8 midpoint codes {stats['fp8_mid']}/{stats['fp8_codes']}")
+
+
+def test_fp8_dedupe_equal_plain(gpu):
+    """Shared block-rows with fp8 maps: the output through the aliases equals the
+    plain fp8 output bit for bit."""
+    wl = _multiturn([600, 1000, 130, 900, 420], Hs=4, Ht=6, Hkv=3)
+    B = wl.spec.B
+    q, k = to_dev_qk(wl, gpu)
+    m0 = mf.mf_compress_topp(q, k, wl.cu_seqlens, B, wl.spec.p, wl.bias(), tile_format="mxfp8")
+    alias = mf.mf_prefix_dedupe(q, k, wl.cu_seqlens, B)
+    m1 = mf.mf_compress_topp(q, k, wl.cu_seqlens, B, wl.spec.p, wl.bias(), row_alias=alias,
+                             tile_format="mxfp8")
+    (st0, n0), (st1, n1) = mf.mf_read_status(m0), mf.mf_read_status(m1)
+    assert st0 == mf.MF_OK and st1 == mf.MF_OK and n1 < n0
     Wt, vd = torch.from_numpy(wl.W).to(gpu), to_dev_v(wl, gpu)
     O0 = mf.mf_apply_translated(m0, Wt, vd, wl.cu_seqlens)
     O1 = mf.mf_apply_translated(m1, Wt, vd, wl.cu_seqlens)
