@@ -11,6 +11,7 @@ one sequence of 32768 tokens, 32 source heads -> 64 target heads, d = 128,
 B = 128, p = 0.95, bf16 Q/K/V, each target mixing 4 sources (Dirichlet weights).
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+                  [--config N] [--dedupe] [--tile-format bf16|mxfp8]
 """
 from __future__ import annotations
 
@@ -59,12 +60,13 @@ def traffic_record(kernel: str, workload: str):
     return r.get("bytes_per_launch")
 
 
-def algorithmic_bytes(wl, nnz: int) -> dict:
+def algorithmic_bytes(wl, nnz: int, tile_format: str = "bf16") -> dict:
     s = wl.spec
     T, NBR = wl.T, sum((L + s.B - 1) // s.B for L in wl.lens)
     e_qk = 4 if s.qk_dtype == "fp32" else 2
     meta = (s.Hs * NBR + 1) * 8 + s.Hs * T * 4          # row_ptr + kept mass
-    tiles = nnz * (s.B * s.B * 2 + 4)                    # bf16 tiles + col_idx
+    tile = s.B * s.B * 2 if tile_format == "bf16" else s.B * s.B + s.B * (s.B // 32)
+    tiles = nnz * (tile + 4)                             # tiles + col_idx
     compress = 2 * s.Hs * T * s.d * e_qk + tiles + meta
     apply = tiles + meta + s.Hkv * T * s.d * 2 + s.Ht * s.Hs * 4 + s.Ht * T * s.d * 4
     return dict(compress=compress, apply=apply)
@@ -113,6 +115,8 @@ def main():
     ap.add_argument("--dedupe", action="store_true",
                     help="share block-rows whose q/k prefix repeats an earlier sequence's "
                          "(mf_prefix_dedupe inside every step; multi-turn workload 5)")
+    ap.add_argument("--tile-format", choices=("bf16", "mxfp8"), default="bf16",
+                    help="map tiles: bf16, or block-scaled E4M3 (half the tile bytes)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (HBM counter scale)")
     args = ap.parse_args()
@@ -147,7 +151,7 @@ def main():
     W = torch.from_numpy(wl.W).to(dev)
     cu = wl.cu_seqlens
     cu_dev = torch.from_numpy(cu).to(dev)
-    m = mf.alloc_map(s.Hs, cu, s.B, dev)
+    m = mf.alloc_map(s.Hs, cu, s.B, dev, tile_format=args.tile_format)
     ws_c = torch.empty(mf.mf_compress_workspace_bytes(s.Hs, cu, s.B, s.d), dtype=torch.uint8, device=dev)
     ws_a = torch.empty(mf.mf_apply_workspace_bytes(s.Hkv, cu, s.B, s.d), dtype=torch.uint8, device=dev)
     O = torch.empty((s.Ht, wl.T, s.d), dtype=torch.float32, device=dev)
@@ -199,8 +203,8 @@ def main():
     t_apply = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
     log(f"ms/step {ms_step:.3f}  compress {t_comp:.3f} ms  apply {t_apply:.3f} ms")
 
-    ab = algorithmic_bytes(wl, nnz)
-    workload = f"workload{args.config}"
+    ab = algorithmic_bytes(wl, nnz, args.tile_format)
+    workload = f"workload{args.config}" + ("" if args.tile_format == "bf16" else f"_{args.tile_format}")
     achieved = ab["apply"] / (t_apply * 1e-3) / 1e9
     traffic = traffic_record("mf_apply_translated", workload)
     roof = dict(kernel="mf_apply_translated (fused retrieval)", bound="hbm", achieved=round(achieved, 1),
@@ -222,7 +226,8 @@ def main():
         shared = int((a != np.arange(len(a))).sum())
         log(f"dedupe: {shared} of {len(a)} block-rows share an earlier one")
     line = {
-        "metric": ("compressed-map prefill tokens/s at L=32K (compress+apply)" if args.config == 4
+        "metric": ("compressed-map prefill tokens/s at L=32K (compress+apply)"
+                   if args.config == 4 and args.tile_format == "bf16"
                    else "compressed-map prefill tokens/s (compress+apply)"),
         "value": round(wl.T / (ms_step * 1e-3), 1),
         "unit": "tokens/s",
@@ -237,7 +242,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": s.name, "tokens": wl.T, "source_heads": s.Hs, "target_heads": s.Ht,
                    "v_heads": s.Hkv, "head_dim": s.d, "block": s.B, "top_p": s.p,
-                   "kept_tiles": nnz, "prefix_dedupe": bool(args.dedupe),
+                   "kept_tiles": nnz, "tile_format": args.tile_format,
+                   "prefix_dedupe": bool(args.dedupe),
                    "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -5,8 +5,8 @@
  *
  *   mf_compress_topp        sender side: attention map of every source head,
  *                           block-level top-p selection, kept blocks written as
- *                           bf16 probability tiles in Block Sparse Row (BSR) form
- *                           with per-row kept mass.
+ *                           bf16 (or block-scaled fp8) probability tiles in Block
+ *                           Sparse Row (BSR) form with per-row kept mass.
  *                           MapFlow ("Accelerating Cross-Model LLM Inference via
  *                           Attention Map Reuse"), §4 (top-p compression into
  *                           BSR) and §5.2 (Attention State Compressor).
