@@ -72,6 +72,27 @@ def algorithmic_bytes(wl, nnz: int, tile_format: str = "bf16") -> dict:
     return dict(compress=compress, apply=apply)
 
 
+def mfma_flops(torch, wl, m, W, nnz: int) -> dict:
+    """Algorithmic MFMA work: compress = one QK^T over every causal tile of every
+    source head; apply = one (B x B) x (B x d) product per target, query block and
+    key block in the union of the target's sources' kept blocks."""
+    s = wl.spec
+    NBR = m.num_block_rows
+    nbs = [(L + s.B - 1) // s.B for L in wl.lens]
+    tri = sum(n * (n + 1) // 2 for n in nbs)
+    compress = 2.0 * s.d * s.B * s.B * s.Hs * tri
+    dev = m.row_ptr.device
+    rp = m.row_ptr
+    rows = torch.repeat_interleave(torch.arange(s.Hs * NBR, device=dev), rp[1:] - rp[:-1])
+    kept = torch.zeros((s.Hs, NBR, max(nbs)), dtype=torch.bool, device=dev)
+    kept[rows // NBR, rows % NBR, m.col_idx[:nnz].long()] = True
+    if m.row_alias is not None:
+        kept = kept[:, m.row_alias.long()]
+    nz = (W != 0)
+    blocks = sum(int(kept[nz[t]].any(dim=0).sum()) for t in range(W.shape[0]))
+    return dict(compress=compress, apply=2.0 * s.B * s.B * s.d * blocks)
+
+
 def cpu_baseline(wl, rows):
     """The fp64 oracle on a bounded sample of block-rows (all heads, all targets),
     scaled to the whole workload by the share of causal key blocks the sample covers."""
@@ -204,14 +225,19 @@ def main():
     log(f"ms/step {ms_step:.3f}  compress {t_comp:.3f} ms  apply {t_apply:.3f} ms")
 
     ab = algorithmic_bytes(wl, nnz, args.tile_format)
+    fl = mfma_flops(torch, wl, m, W, nnz)
     workload = f"workload{args.config}" + ("" if args.tile_format == "bf16" else f"_{args.tile_format}")
     achieved = ab["apply"] / (t_apply * 1e-3) / 1e9
     traffic = traffic_record("mf_apply_translated", workload)
     roof = dict(kernel="mf_apply_translated (fused retrieval)", bound="hbm", achieved=round(achieved, 1),
                 peak=HBM_PEAK_GBS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
                 algorithmic_bytes=int(ab["apply"]), ms_per_launch=round(t_apply, 4),
+                mfma_tflops=round(fl["apply"] / (t_apply * 1e-3) / 1e12, 1),
+                mfma_frac=round(fl["apply"] / (t_apply * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                 compress_ms=round(t_comp, 4),
-                compress_gbs=round(ab["compress"] / (t_comp * 1e-3) / 1e9, 1))
+                compress_gbs=round(ab["compress"] / (t_comp * 1e-3) / 1e9, 1),
+                compress_mfma_tflops=round(fl["compress"] / (t_comp * 1e-3) / 1e12, 1),
+                compress_mfma_frac=round(fl["compress"] / (t_comp * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4))
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -10,7 +10,8 @@ Definitions followed: MapFlow ("Accelerating Cross-Model LLM Inference via
 Attention Map Reuse") §4 and §5.2 for block top-p retention in BSR form, §3.3
 and §5.4 for the linear head mix applied to the receiver's values; the
 AttnCache guide ("AttnCache Guide: Reusing Attention Maps in LLM Prefill"),
-section "The Quadratic Self-Attention Cost", for the softmax attention map.
+section "The Quadratic Self-Attention Cost", for the softmax attention map;
+MapFlow §3.3 for the total-variation distance used to pick recomputed layers.
 The subset rule (smallest subset reaching p of the row mass, largest mass
 among those, lowest indices among equal masses) is the reading of "top-p
 blocks" taken in the oracle's header.
@@ -108,4 +109,26 @@ def bf_apply(per_src: Dict[int, Dict[int, dict]], W: Sequence[Sequence[float]], 
                     for c in range(d):
                         terms[c].append(scale * a * float(v[j][c]))
         out[i] = [math.fsum(x) for x in terms]
+    return out
+
+
+def bf_tv(per_src: Dict[int, Dict[int, dict]], W: Sequence[Sequence[float]], t: int,
+          A_r: List[List[float]], B: int, renorm: bool = True) -> List[float]:
+    """TV_t[i] = 1/2 sum_j |A~_t[i][j] - A_r[i][j]|, A~ built element by element."""
+    L = len(A_r)
+    out = []
+    for i in range(L):
+        I = i // B
+        mix = [[] for _ in range(L)]
+        for h, rows in per_src.items():
+            w = float(W[t][h])
+            if w == 0.0:
+                continue
+            r = rows[I]
+            km = r["kmass"][i - I * B]
+            scale = (w / km if km > 0 else 0.0) if renorm else w
+            for J in r["kept"]:
+                for j in range(J * B, min((J + 1) * B, L)):
+                    mix[j].append(scale * r["A"][i][j])
+        out.append(0.5 * math.fsum(abs(math.fsum(mix[j]) - A_r[i][j]) for j in range(L)))
     return out

@@ -36,6 +36,13 @@ What it computes, and where that is stated:
 * fp8 tiles (optional).  MapFlow §9 names quantised sparse maps as the way to
   shrink them further; `codec="mxfp8"` in apply reads every kept tile through
   the block-scaled E4M3 codec of oracle/mx_codec.py.
+* Recompute-boundary profiling (MapFlow §3.3: the receiver layers to
+  recompute are chosen offline from layer-wise total-variation distance between
+  the translated map and the receiver's own map).  Reading taken here: per query
+  row, TV_t[i] = 1/2 sum_j |A~_t[i,j] - A_t[i,j]|, where A~_t is the translated
+  map exactly as retrieval uses it (sum_h W[t,h] renorm(A_hat_h), zero outside
+  the kept blocks) and A_t the receiver's causal softmax map from its own q and
+  k (K head g(t) as for V); a layer's score is the mean over rows.
 * Dense attention for recomputed heads (MapFlow §4: the receiver computes its
   first r layers normally): O_h = A_h V_g(h).
 
@@ -371,6 +378,57 @@ def apply(res: Dict[Tuple[int, int, int], RowResult], W: np.ndarray, v: np.ndarr
                 out[(t, s, I)] = np.zeros((n, v.shape[2]))
                 continue
             out[(t, s, I)] = apply_row(src, W, t, v[g, a:a + L], B, renorm, codec)
+    return out
+
+
+def translated_map_row(src_rows: Dict[int, RowResult], W: np.ndarray, t: int, B: int,
+                       renorm: bool = True, codec: Optional[str] = None) -> np.ndarray:
+    """A~_t for one block-row: sum_h W[t,h] * (P^h / kmass^h) on h's kept blocks, 0 elsewhere."""
+    any_row = next(iter(src_rows.values()))
+    out = np.zeros_like(any_row.P)
+    for h, rr in src_rows.items():
+        w = float(W[t, h])
+        if w == 0.0:
+            continue
+        if renorm:
+            with np.errstate(divide="ignore", invalid="ignore"):
+                scale = np.where(rr.kmass > 0, w / rr.kmass, 0.0)
+        else:
+            scale = np.full(len(rr.rows), w)
+        for J in rr.kept:
+            blk = rr.P[:, J * B:(J + 1) * B]
+            if codec == "mxfp8":
+                blk = mx_codec.quantize(rr.tile(J, B))[:blk.shape[0], :blk.shape[1]]
+            out[:, J * B:J * B + blk.shape[1]] += scale[:, None] * blk
+    return out
+
+
+def tv_distance(res: Dict[Tuple[int, int, int], RowResult], W: np.ndarray, q_r: np.ndarray,
+                k_r: np.ndarray, cu: np.ndarray, B: int, bias: dict, renorm: bool = True,
+                targets: Optional[Sequence[int]] = None,
+                rows: Optional[Sequence[Tuple[int, int]]] = None,
+                codec: Optional[str] = None) -> Dict[Tuple[int, int, int], np.ndarray]:
+    """TV_t[i] = 1/2 sum_j |A~_t[i,j] - A_t[i,j]| for the given (target, (seq, block-row)).
+
+    res must hold every source with a nonzero weight for those rows; q_r [Ht][T][d]
+    and k_r [Hkr][T][d] are the receiver's; query head t reads K head g(t).
+    Returns {(t, s, I): TV per row of the block-row}."""
+    Ht, Hs = W.shape
+    Hkr = k_r.shape[0]
+    targets = range(Ht) if targets is None else targets
+    rows = block_rows(cu, B) if rows is None else rows
+    sq = seqs(cu)
+    out = {}
+    for t in targets:
+        g = v_head(t, Ht, Hkr)
+        for (s, I) in rows:
+            a, L = sq[s]
+            r = np.arange(I * B, min((I + 1) * B, L))
+            ncols = min((I + 1) * B, L)
+            A, _ = softmax_rows(logits(q_r[t, a:a + L], k_r[g, a:a + L], r, ncols, bias))
+            src = {h: res[(h, s, I)] for h in range(Hs) if W[t, h] != 0.0}
+            At = translated_map_row(src, W, t, B, renorm, codec) if src else np.zeros_like(A)
+            out[(t, s, I)] = 0.5 * np.sum(np.abs(At - A), axis=1)
     return out
 
 
