@@ -126,6 +126,53 @@ def copy_calibration(torch, nbytes: int = 1 << 30, reps: int = 3):
     print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
 
 
+def tv_bench(torch, mf, wlmod, wl, m, W, cu, cu_dev, args):
+    """Times mf_tv_distance over the whole workload (every target head and row)."""
+    s = wl.spec
+    dev = W.device
+    rq, rk, rqb, rkb = wlmod.receiver_qk(wl)
+    if rqb is not None:
+        qr = torch.from_numpy(rqb.view(np.int16)).to(dev).view(torch.bfloat16)
+        kr = torch.from_numpy(rkb.view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        qr, kr = torch.from_numpy(rq).to(dev), torch.from_numpy(rk).to(dev)
+    del rq, rk, rqb, rkb
+    out = torch.empty((W.shape[0], wl.T), dtype=torch.float32, device=dev)
+    ws = torch.empty(mf.load().mf_tv_distance_workspace_bytes(mf._cu_ptr(mf._cu_host(cu)), len(cu) - 1, s.B),
+                     dtype=torch.uint8, device=dev)
+    for _ in range(max(args.warmup, 1)):
+        mf.mf_tv_distance(m, W, qr, kr, cu, wl.bias(), out=out, workspace=ws, cu_dev=cu_dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        mf.mf_tv_distance(m, W, qr, kr, cu, wl.bias(), out=out, workspace=ws, cu_dev=cu_dev)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms_ev = e0.elapsed_time(e1) / args.steps
+    nbs = [(L + s.B - 1) // s.B for L in wl.lens]
+    tri = sum(n * (n + 1) // 2 for n in nbs)
+    flops = 2 * 2.0 * s.d * s.B * s.B * W.shape[0] * tri     # two Q K^T passes per target
+    log(f"tv: {ms_ev:.3f} ms per call, mean tv {float(out.mean()):.4f}")
+    line = {
+        "metric": "map TV-distance profiling tokens/s (all target heads)",
+        "value": round(wl.T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if s.qk_dtype == "bf16" else "fp32", "data": "synthetic",
+        "config": {"workload": s.name, "tokens": wl.T, "target_heads": int(W.shape[0]),
+                   "tile_format": args.tile_format, "parallelism": "none (1 GPU)"},
+        "roofline": {"kernel": "mf_tv_distance", "bound": "mfma",
+                     "achieved": round(flops / (ms_ev * 1e-3) / 1e12, 1), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(flops / (ms_ev * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "ms_per_launch": round(ms_ev, 4)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -138,6 +185,9 @@ def main():
                          "(mf_prefix_dedupe inside every step; multi-turn workload 5)")
     ap.add_argument("--tile-format", choices=("bf16", "mxfp8"), default="bf16",
                     help="map tiles: bf16, or block-scaled E4M3 (half the tile bytes)")
+    ap.add_argument("--tv", action="store_true",
+                    help="time mf_tv_distance (translated map vs a synthetic receiver's own map) "
+                         "on the compressed map instead of the compress + apply step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (HBM counter scale)")
     args = ap.parse_args()
@@ -202,6 +252,12 @@ def main():
         if st != mf.MF_OK:
             raise SystemExit(f"compression status {st}")
         log(f"warmup done: nnz={nnz} tiles ({nnz / m.capacity:.3f} of causal)")
+
+    if args.tv:
+        if args.warmup == 0:
+            step()
+        tv_bench(torch, mf, wlmod, wl, m, W, cu, cu_dev, args)
+        return
 
     stream = torch.cuda.current_stream()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]

@@ -19,7 +19,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmapflow.so")
-SOURCES = ["mf_rows.hip", "mf_compress.hip", "mf_apply.hip", "mf_dense.hip", "mf_dedupe.hip", "mf_api.hip"]
+SOURCES = ["mf_rows.hip", "mf_compress.hip", "mf_apply.hip", "mf_dense.hip", "mf_dedupe.hip", "mf_tv.hip",
+           "mf_api.hip"]
 ARCH = "gfx950"
 
 

@@ -26,7 +26,7 @@ EXPORTS = ("mf_num_block_rows", "mf_compress_max_tiles", "mf_compress_workspace_
            "mf_compress_topp", "mf_apply_workspace_bytes", "mf_apply_translated",
            "mf_dense_workspace_bytes", "mf_dense_ref_attention", "mf_read_status",
            "mf_status_string", "mf_prefix_dedupe_workspace_bytes", "mf_prefix_dedupe",
-           "mf_tile_bytes")
+           "mf_tile_bytes", "mf_tv_distance_workspace_bytes", "mf_tv_distance")
 
 
 class MfLogitBias(ctypes.Structure):
@@ -80,6 +80,9 @@ def load():
         "mf_prefix_dedupe_workspace_bytes": (sz, [pcu, i32, i32]),
         "mf_prefix_dedupe": (i32, [vp, vp, vp, i32, pcu, vp, i32, i32, i32, i32, vp, vp, sz]),
         "mf_tile_bytes": (i64, [i32, i32]),
+        "mf_tv_distance_workspace_bytes": (sz, [pcu, i32, i32]),
+        "mf_tv_distance": (i32, [vp, ctypes.POINTER(MfBsrMap), vp, i32, vp, vp, i32, i32, i32, pcu,
+                                 vp, i32, ctypes.POINTER(MfLogitBias), i32, vp, vp, sz]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -317,6 +320,37 @@ def mf_apply_translated(m: BsrMap, W: torch.Tensor, v: torch.Tensor, cu_seqlens,
                                  _cu_ptr(cu), cu_dev.data_ptr(), len(cu) - 1, int(bool(renorm)),
                                  out.data_ptr(), workspace.data_ptr(), workspace.numel())
     _check("mf_apply_translated", st)
+    return out
+
+
+def mf_tv_distance(m: BsrMap, W: torch.Tensor, q: torch.Tensor, k: torch.Tensor, cu_seqlens,
+                   bias: Optional[dict] = None, renorm: bool = True,
+                   out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                   cu_dev: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """[Ht, T] fp32: 1/2 sum_j |translated - receiver| per query row; q [Ht, T, d] and
+    k [Hkr, T, d] are the receiver's."""
+    lib = load()
+    cu = _cu_host(cu_seqlens)
+    Ht, T, d = q.shape
+    Hkr = k.shape[0]
+    if k.dtype != q.dtype or k.shape[1:] != q.shape[1:] or not (q.is_contiguous() and k.is_contiguous()):
+        raise ValueError("q and k must be contiguous, of one dtype, [H, T, d]")
+    if W.dtype != torch.float32 or not W.is_contiguous() or tuple(W.shape) != (Ht, m.num_heads):
+        raise ValueError("W must be contiguous float32 [Ht, Hs]")
+    dev = q.device
+    if out is None:
+        out = torch.empty((Ht, T), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(lib.mf_tv_distance_workspace_bytes(_cu_ptr(cu), len(cu) - 1, m.block),
+                                dtype=torch.uint8, device=dev)
+    if cu_dev is None:
+        cu_dev = _dev_cu(cu, dev)
+    cs = m.cstruct()
+    st = lib.mf_tv_distance(_stream(), ctypes.byref(cs), W.data_ptr(), Ht, q.data_ptr(), k.data_ptr(),
+                            _dtype_code(q), Hkr, d, _cu_ptr(cu), cu_dev.data_ptr(), len(cu) - 1,
+                            _bias(bias), int(bool(renorm)), out.data_ptr(), workspace.data_ptr(),
+                            workspace.numel())
+    _check("mf_tv_distance", st)
     return out
 
 

@@ -191,3 +191,28 @@ def small_variant(index: int, lens: List[int], seed: Optional[int] = None,
             kw["w_var"] = 1.0 / kw["Hs"]
         s = dataclasses.replace(s, **kw)
     return make_workload(s, seed=seed, lens=lens)
+
+
+def receiver_qk(wl: Workload, Hkr: Optional[int] = None, alpha: float = 0.9,
+                seed: Optional[int] = None):
+    """A receiver model's queries [Ht][T][d] and keys [Hkr][T][d] for map-distance
+    profiling: each receiver head leans on the sender head with the largest weight in
+    its row of W (alpha times that head's q or k plus sqrt(1 - alpha^2) times fresh
+    N(0,1) noise), so the two models' maps are related but not equal.  Rounded to bf16
+    for bf16 workloads.  Returns (q, k, q_bits, k_bits); the bits are None for fp32."""
+    s = wl.spec
+    Ht = wl.W.shape[0]
+    Hkr = Ht if Hkr is None else Hkr
+    rng = np.random.default_rng((s.seed if seed is None else seed) + 7919)
+    top = np.argmax(np.abs(wl.W), axis=1)
+    beta = np.float32(np.sqrt(1.0 - alpha * alpha))
+    q = np.empty((Ht, wl.T, s.d), dtype=np.float32)
+    k = np.empty((Hkr, wl.T, s.d), dtype=np.float32)
+    for t in range(Ht):
+        q[t] = np.float32(alpha) * wl.q[top[t]] + beta * _normal(rng, (wl.T, s.d))
+    for g in range(Hkr):
+        k[g] = np.float32(alpha) * wl.k[top[g * (Ht // Hkr)]] + beta * _normal(rng, (wl.T, s.d))
+    if s.qk_dtype == "bf16":
+        qb, kb = f32_to_bf16_bits(q), f32_to_bf16_bits(k)
+        return bf16_bits_to_f32(qb), bf16_bits_to_f32(kb), qb, kb
+    return q, k, None, None

@@ -19,6 +19,9 @@
  *                           both sides read the first copy.  MapFlow §5.3 (Block
  *                           Manager: blocks indexed by prefix hashes), §2.3
  *                           (prefix caching).
+ *   mf_tv_distance          per-row total-variation distance between the
+ *                           translated map and a receiver's own map, to choose
+ *                           the receiver layers to recompute (MapFlow §3.3).
  *   mf_dense_ref_attention  softmax(Q K^T / sqrt(d) + bias) V, causal, for the
  *                           receiver layers that are recomputed (MapFlow §4) and
  *                           the exact path a cache miss falls back to (AttnCache
@@ -268,6 +271,34 @@ mf_status mf_dense_ref_attention(void *stream, const void *q, const void *k, con
                                  const int32_t *cu_seqlens_host, const int32_t *cu_seqlens_dev,
                                  int32_t nseq, const mf_logit_bias *bias, float *o,
                                  void *workspace, size_t workspace_bytes);
+
+/* Device workspace bytes mf_tv_distance needs (0 if the arguments are invalid). */
+size_t mf_tv_distance_workspace_bytes(const int32_t *cu_seqlens_host, int32_t nseq, int32_t B);
+
+/* Total-variation distance between the translated map and a receiver's own map,
+ * per query row, for choosing which receiver layers to recompute (MapFlow §3.3:
+ * layer-wise TV distance profiled offline).
+ *
+ *   tv[t][i] = 1/2 sum_j | A~_t[i,j] - A_t[i,j] |
+ *
+ * A~_t is the translated map exactly as mf_apply_translated uses it
+ * (sum_h W[t,h] A_hat_h[i,j] / kmass_h[i] with `renorm`, W[t,h] A_hat_h[i,j]
+ * without; zero outside the kept blocks); A_t is the receiver's causal
+ * softmax(q_t k_g(t)^T / sqrt(d) + bias), g(t) = floor(t * Hkr / Ht).  Neither
+ * map is materialised.  A layer's score is the mean of tv over rows and heads.
+ *
+ * map         compressed sender map (either tile format); read only.
+ * W           [Ht][Hs] fp32, device.
+ * q, k        receiver queries [Ht][T][d] and keys [Hkr][T][d], dtype qk_dtype.
+ * bias        host, may be NULL: the receiver's logit offsets.
+ * tv          [Ht][T] fp32, device, written for every token.
+ * workspace   device, at least mf_tv_distance_workspace_bytes(...) bytes.
+ * Errors: MF_ERR_INVALID_ARG, MF_ERR_UNSUPPORTED, MF_ERR_WORKSPACE, MF_ERR_HIP. */
+mf_status mf_tv_distance(void *stream, const mf_bsr_map *map, const float *W, int32_t Ht,
+                         const void *q, const void *k, mf_dtype qk_dtype, int32_t Hkr, int32_t d,
+                         const int32_t *cu_seqlens_host, const int32_t *cu_seqlens_dev,
+                         int32_t nseq, const mf_logit_bias *bias, int32_t renorm, float *tv,
+                         void *workspace, size_t workspace_bytes);
 
 /* Waits for `stream`, then returns the map's device status (MF_OK or
  * MF_ERR_CAPACITY) and, if nnz_out is not NULL, stores the kept-tile count

@@ -30,7 +30,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = header_functions()
-    assert len(names) == 13
+    assert len(names) == 15
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(mf.EXPORTS) == names
@@ -139,6 +139,24 @@ def test_unknown_tile_format_rejected(lib):
     m = mf.MfBsrMap(2, 32, 4, 100, 10, 8, 8, 8, 8, 8, 8, None, 5)
     assert lib.mf_apply_translated(None, ctypes.byref(m), fake, 4, fake, 2, 64, pc, fake, 1, 1,
                                    fake, fake, 1 << 40) == mf.MF_ERR_INVALID_ARG
+
+
+def test_tv_distance_rejects_bad_arguments(lib):
+    c = cu([100])
+    fake = ctypes.c_void_p(16)
+    pc = c.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    need = lib.mf_tv_distance_workspace_bytes(pc, 1, 32)
+    assert need > 0 and lib.mf_tv_distance_workspace_bytes(pc, 1, 48) == 0
+    m = mf.MfBsrMap(2, 32, 4, 100, 10, 8, 8, 8, 8, 8, 8, None, 0)
+    f = lib.mf_tv_distance
+    args = lambda Ht=4, Hkr=2, dt=0, d=64, ws=need: (None, ctypes.byref(m), fake, Ht, fake, fake, dt, Hkr, d,
+                                                      pc, fake, 1, None, 1, fake, fake, ws)
+    assert f(*args(Hkr=3)) == mf.MF_ERR_INVALID_ARG
+    assert f(*args(d=80)) == mf.MF_ERR_UNSUPPORTED
+    assert f(*args(dt=5)) == mf.MF_ERR_UNSUPPORTED
+    assert f(*args(ws=need - 1)) == mf.MF_ERR_WORKSPACE
+    m.num_block_rows = 5
+    assert f(*args()) == mf.MF_ERR_INVALID_ARG
 
 
 def test_status_strings(lib):

@@ -431,3 +431,82 @@ def test_fp8_dedupe_equal_plain(gpu):
     O0 = mf.mf_apply_translated(m0, Wt, vd, wl.cu_seqlens)
     O1 = mf.mf_apply_translated(m1, Wt, vd, wl.cu_seqlens)
     assert torch.equal(O0, O1)
+
+
+# ---------------------------------------------------------------------------
+# total-variation distance (recompute-boundary profiling)
+# ---------------------------------------------------------------------------
+
+def _tv_tol(W, t):
+    """bf16 rounding (nearest even, 8 significand bits) moves each translated value by
+    at most 2^-8 of it, so the summed absolute difference moves by at most
+    2^-8 sum_h |W[t,h]| (renormalised kept rows sum to 1), and TV by half that; fp32
+    probabilities add about 1e-5."""
+    return 2.0 ** -9 * float(np.abs(W[t]).sum()) + 2e-5
+
+
+def _receiver_dev(rq, rk, rqb, rkb, dev):
+    if rqb is None:
+        return torch.from_numpy(rq).to(dev), torch.from_numpy(rk).to(dev)
+    return (torch.from_numpy(rqb.view(np.int16)).to(dev).view(torch.bfloat16),
+            torch.from_numpy(rkb.view(np.int16)).to(dev).view(torch.bfloat16))
+
+
+@pytest.mark.parametrize("idx,lens,kw,Hkr,fmt", [
+    (2, [700], dict(Hs=6, Ht=6, Hkv=6), 6, "bf16"),
+    (3, [777], dict(Hs=6, Ht=8, Hkv=2), 2, "bf16"),
+    (4, [1100], dict(Hs=8, Ht=16, Hkv=16), 16, "bf16"),
+    (5, [300, 520, 64, 1, 129, 0, 700], dict(Hs=4, Ht=4, Hkv=4), 4, "bf16"),
+    (1, None, {}, 2, "bf16"),
+    (4, [900], dict(Hs=8, Ht=16, Hkv=16), 8, "mxfp8"),
+    (5, [300, 520, 64, 1, 129, 0, 700], dict(Hs=4, Ht=4, Hkv=4), 2, "mxfp8"),
+])
+def test_tv_distance_small(gpu, idx, lens, kw, Hkr, fmt):
+    """Per-row TV distance against the oracle on every block-row (rows at an
+    ambiguous top-p cut excluded), with receiver heads sharing K heads (GQA)."""
+    wl = wlmod.make_config(1) if lens is None else wlmod.small_variant(idx, lens, **kw)
+    B = wl.spec.B
+    say(f"tv {wl.spec.name} lens={wl.lens[:8]} Hkr={Hkr} tiles={fmt}")
+    m, st, nnz = gpu_compress(wl, gpu, tile_format=fmt)
+    assert st == mf.MF_OK
+    rq, rk, rqb, rkb = wlmod.receiver_qk(wl, Hkr)
+    qd, kd = _receiver_dev(rq, rk, rqb, rkb, gpu)
+    Wt = torch.from_numpy(np.ascontiguousarray(wl.W)).to(gpu)
+    tv = mf.mf_tv_distance(m, Wt, qd, kd, wl.cu_seqlens, wl.bias()).cpu().numpy()
+    res = orc.compress(wl.q, wl.k, wl.cu_seqlens, B, wl.spec.p, wl.bias())
+    stats = check_rows(HostMap(m), res, wl.cu_seqlens, wl.T)
+    flips = {(s, I) for (h, s, I) in stats["flips"]}
+    ref = orc.tv_distance(res, wl.W, rq, rk, wl.cu_seqlens, B, wl.bias(),
+                          codec="mxfp8" if fmt == "mxfp8" else None)
+    worst, mean = 0.0, []
+    for (t, s, I), v in ref.items():
+        if (s, I) in flips:
+            continue
+        a = int(wl.cu_seqlens[s]) + I * B
+        g = tv[t, a:a + len(v)]
+        e = float(np.max(np.abs(g - v))) if len(v) else 0.0
+        worst = max(worst, e)
+        mean.append(v)
+        assert e <= _tv_tol(wl.W, t), f"tv {(t, s, I)}: max error {e}"
+    mean = float(np.concatenate(mean).mean())
+    say(f"  max |tv - oracle| {worst:.2e}, mean tv {mean:.3f}, flipped block-rows {len(flips)}")
+    assert 0.0 < mean < 1.5
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "mxfp8"])
+def test_tv_self_is_one_minus_kept_mass_full_size(gpu, fmt):
+    """Long-context workload at full size, receiver = sender, W = I: the distance of
+    a renormalised kept row to its full row is 1 - kept mass, exactly; the GPU's TV
+    must match 1 - the GPU's own kept mass within the tiles' rounding."""
+    wl = wlmod.make_config(4)
+    B, Hs = wl.spec.B, wl.spec.Hs
+    m, st, nnz = gpu_compress(wl, gpu, tile_format=fmt)
+    assert st == mf.MF_OK
+    q, k = to_dev_qk(wl, gpu)
+    Wt = torch.eye(Hs, dtype=torch.float32, device=gpu)
+    tv = mf.mf_tv_distance(m, Wt, q, k, wl.cu_seqlens, wl.bias())
+    e = (tv - (1.0 - m.kept_mass)).abs()
+    # half the codec's relative rounding: 2^-8 for bf16, 2^-4 for E4M3
+    tol = 2.0 ** -9 + 2e-5 if fmt == "bf16" else 2.0 ** -5 + 2e-5
+    say(f"full workload 4 tv {fmt}: mean tv {float(tv.mean()):.4f}, max |tv - (1 - kmass)| {float(e.max()):.2e}")
+    assert float(e.max()) <= tol
