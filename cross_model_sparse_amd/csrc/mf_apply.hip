@@ -28,23 +28,47 @@ constexpr int kXcds = 8;
 constexpr int kBufferFlags = 0x00020000;  // buffer descriptor word 3 for raw dword loads
 
 // ---------------------------------------------------------------------------
-// V [Hkv][T][D] -> Vt [Hkv][D][NBR * B], zero past each sequence end
+// V -> Vt [Hkv][D][NBR * B], zero past each sequence end.
+//
+// V is either contiguous [Hkv][T][D] or paged: token j of sequence s lives in
+// page block_table[s][j / P] of a pool [pages][Hkv][P][D] at slot j % P (page
+// indices outside the pool read as zeros).  With query windows (chunked prefill)
+// only key blocks below the window's end are staged: no other block is read.
 // ---------------------------------------------------------------------------
+struct VSrc {
+  const uint16_t *v;          // contiguous V, or null
+  const uint16_t *pages;      // paged pool, or null
+  const int32_t *table;       // [nseq][max_pages]
+  int32_t page_size, max_pages, num_pages, Hkv;
+  const int32_t *window;      // [nseq][2] query tokens [begin, end), or null
+};
+
 template <int B, int D>
-__global__ __launch_bounds__(256) void k_vtranspose(const uint16_t *__restrict__ v, int64_t T,
+__global__ __launch_bounds__(256) void k_vtranspose(VSrc vs, int64_t T,
                                                     const RowInfo *__restrict__ rows, int32_t NBR,
                                                     uint16_t *__restrict__ vt) {
   constexpr int P = B + 8;  // LDS row pitch in elements
   __shared__ __attribute__((aligned(16))) uint16_t t[D * P];
   const int gr = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
   const RowInfo ri = rows[gr];
+  if (vs.window && ri.blk * B >= vs.window[2 * ri.seq + 1]) return;  // not a key of the window
   const int nval = min(B, ri.len - ri.blk * B);
   const int64_t tok0 = (int64_t)ri.start + (int64_t)ri.blk * B;
-  const uint16_t *src = v + ((int64_t)g * T + tok0) * D;
   for (int idx = tid; idx < B * D / 8; idx += 256) {
     const int j = idx / (D / 8), c = idx % (D / 8);
     u32x4 x = u32x4{0u, 0u, 0u, 0u};
-    if (j < nval) x = *reinterpret_cast<const u32x4 *>(src + (int64_t)j * D + c * 8);
+    if (j < nval) {
+      const uint16_t *row = nullptr;
+      if (vs.pages) {
+        const int js = ri.blk * B + j;  // token index inside the sequence
+        const int pg = vs.table[(int64_t)ri.seq * vs.max_pages + js / vs.page_size];
+        if (pg >= 0 && pg < vs.num_pages)
+          row = vs.pages + (((int64_t)pg * vs.Hkv + g) * vs.page_size + js % vs.page_size) * D;
+      } else {
+        row = vs.v + ((int64_t)g * T + tok0 + j) * D;
+      }
+      if (row) x = *reinterpret_cast<const u32x4 *>(row + c * 8);
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       t[(c * 8 + 2 * e) * P + j] = (uint16_t)(x[e] & 0xffffu);
@@ -58,6 +82,44 @@ __global__ __launch_bounds__(256) void k_vtranspose(const uint16_t *__restrict__
     const int d = idx / (B / 8), c = idx % (B / 8);
     *reinterpret_cast<u32x4 *>(dst + (int64_t)d * tpad + c * 8) =
         *reinterpret_cast<const u32x4 *>(&t[d * P + c * 8]);
+  }
+}
+
+// Schedule of the block-rows inside the query windows, in the longest-first
+// order of the full schedule (stable compaction, one work-group).
+__global__ __launch_bounds__(1024) void k_window_sched(const RowInfo *__restrict__ rows,
+                                                       const int32_t *__restrict__ sched,
+                                                       int32_t NBR, int32_t B,
+                                                       const int32_t *__restrict__ window,
+                                                       int32_t *__restrict__ wsched) {
+  __shared__ int32_t wsum[16];
+  __shared__ int32_t base;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) base = 0;
+  __syncthreads();
+  for (int p0 = 0; p0 < NBR; p0 += 1024) {
+    const int p = p0 + tid;
+    int gr = -1;
+    bool keep = false;
+    if (p < NBR) {
+      gr = sched[p];
+      const RowInfo ri = rows[gr];
+      const int a = ri.blk * B;
+      keep = a >= window[2 * ri.seq] && a < window[2 * ri.seq + 1];
+    }
+    const uint64_t mask = wave_ballot(keep);
+    if (lane == 0) wsum[wave] = __popcll(mask);
+    __syncthreads();
+    int off = base;
+    for (int w = 0; w < wave; ++w) off += wsum[w];
+    if (keep) wsched[off + lanes_below(mask)] = gr;
+    __syncthreads();
+    if (tid == 0) {
+      int tot = 0;
+      for (int w = 0; w < 16; ++w) tot += wsum[w];
+      base += tot;
+    }
+    __syncthreads();
   }
 }
 
@@ -362,8 +424,8 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(4))) void
     const char *__restrict__ tiles, const float *__restrict__ kept_mass, int32_t Hs,
     int32_t NBR, int64_t T, const float *__restrict__ W, int32_t Ht, int32_t grp,
     const uint16_t *__restrict__ vt, const RowInfo *__restrict__ rows,
-    const int32_t *__restrict__ sched, int32_t nbw, int64_t capacity, int32_t renorm,
-    float *__restrict__ o, const int32_t *__restrict__ row_alias) {
+    const int32_t *__restrict__ sched, int32_t nrows, int32_t nbw, int64_t capacity,
+    int32_t renorm, float *__restrict__ o, const int32_t *__restrict__ row_alias) {
   using C = Apply4Cfg<B, D, FMT>;
   constexpr int KU = C::KU, NP = C::NP, NR = C::NR, TB = C::TB, DQ = C::DQ;
   constexpr bool FP8 = FMT == MF_TILE_MXFP8;
@@ -378,7 +440,7 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(4))) void
   const int m16 = lane & 15, kg = lane >> 4;
   int pos, t;
   xcd_map(Ht, pos, t);
-  if (pos >= NBR) return;
+  if (pos >= nrows) return;
   const int gr = sched[pos];
   const RowInfo ri = rows[gr];
   const int I = ri.blk, L = ri.len;
@@ -647,8 +709,8 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(2))) void
     const char *__restrict__ tiles, const float *__restrict__ kept_mass, int32_t Hs,
     int32_t NBR, int64_t T, const float *__restrict__ W, int32_t Ht, int32_t grp,
     const uint16_t *__restrict__ vt, const RowInfo *__restrict__ rows,
-    const int32_t *__restrict__ sched, int32_t nbw, int64_t capacity, int32_t renorm,
-    float *__restrict__ o, const int32_t *__restrict__ row_alias) {
+    const int32_t *__restrict__ sched, int32_t nrows, int32_t nbw, int64_t capacity,
+    int32_t renorm, float *__restrict__ o, const int32_t *__restrict__ row_alias) {
   using C = ApplyMixCfg<B, D, FMT>;
   constexpr int G = C::G, KC = C::KC, SB = C::SB, NP = C::NP;
   constexpr bool FP8 = FMT == MF_TILE_MXFP8;
@@ -680,7 +742,7 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(2))) void
   const int x = blockIdx.x % kXcds, kx = blockIdx.x / kXcds;
   const int round = kx / ngrp, tg = kx % ngrp;
   const int pos = round * kXcds + ((round & 1) ? (kXcds - 1 - x) : x);
-  if (pos >= NBR) return;
+  if (pos >= nrows) return;
   const int gr = sched[pos];
   const RowInfo ri = rows[gr];
   const int I = ri.blk, L = ri.len;
@@ -966,12 +1028,13 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(2))) void
   }
 }
 
-// The two apply kernels for one tile format.
+// The two apply kernels for one tile format, over `nrows` block-rows of `sched`.
 template <int B, int D, int FMT>
 static mf_status launch_apply_fmt(hipStream_t s, const mf_bsr_map *map, const float *W, int32_t Ht,
                                   int32_t Hkv, const SeqGeom &g, int32_t renorm, float *o,
-                                  void *ws, const VtWs &w, int nbw, size_t smem, size_t smem_mix,
-                                  size_t vbufs, size_t vbufs_mix) {
+                                  void *ws, const VtWs &w, const int32_t *sched, int32_t nrows,
+                                  int nbw, size_t smem, size_t smem_mix, size_t vbufs,
+                                  size_t vbufs_mix) {
   using CM = ApplyMixCfg<B, D, FMT>;
   if (smem + vbufs > 64 * 1024 &&
       hipFuncSetAttribute(reinterpret_cast<const void *>(&k_apply4<B, D, FMT>),
@@ -982,28 +1045,28 @@ static mf_status launch_apply_fmt(hipStream_t s, const mf_bsr_map *map, const fl
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem_mix) != hipSuccess)
     return MF_ERR_HIP;
   const char *tiles = static_cast<const char *>(map->tiles);
-  const int64_t npos = ((int64_t)g.NBR + kXcds - 1) / kXcds * kXcds;
+  const int64_t npos = ((int64_t)nrows + kXcds - 1) / kXcds * kXcds;
   // one launch per source-count class; a work-group whose targets are all of
   // the other class returns right after reading their weight rows
   hipLaunchKernelGGL((k_apply4<B, D, FMT>), dim3((unsigned)(npos * Ht)),
                      dim3(Apply4Cfg<B, D, FMT>::NT), smem, s, map->row_ptr, map->col_idx, tiles,
                      map->kept_mass, map->num_heads, g.NBR, g.T, W, Ht, Ht / Hkv,
-                     at<uint16_t>(ws, w.vt), at<RowInfo>(ws, w.rt.rows),
-                     at<int32_t>(ws, w.rt.sched), nbw, map->capacity_tiles, renorm, o,
-                     map->row_alias);
+                     at<uint16_t>(ws, w.vt), at<RowInfo>(ws, w.rt.rows), sched, nrows, nbw,
+                     map->capacity_tiles, renorm, o, map->row_alias);
   if (hip_status() != MF_OK) return MF_ERR_HIP;
   const int64_t ngrp = (Ht + CM::G - 1) / CM::G;
   hipLaunchKernelGGL((k_apply_mix<B, D, FMT>), dim3((unsigned)(npos * ngrp)), dim3(CM::NT),
                      smem_mix, s, map->row_ptr, map->col_idx, tiles, map->kept_mass,
                      map->num_heads, g.NBR, g.T, W, Ht, Ht / Hkv, at<uint16_t>(ws, w.vt),
-                     at<RowInfo>(ws, w.rt.rows), at<int32_t>(ws, w.rt.sched), nbw,
-                     map->capacity_tiles, renorm, o, map->row_alias);
+                     at<RowInfo>(ws, w.rt.rows), sched, nrows, nbw, map->capacity_tiles, renorm,
+                     o, map->row_alias);
   return hip_status();
 }
 
+// V staging, the window schedule (if any), then both apply kernels.
 template <int B, int D>
 static mf_status launch_apply(hipStream_t s, const mf_bsr_map *map, const float *W, int32_t Ht,
-                              const void *v, int32_t Hkv, const SeqGeom &g, int32_t renorm,
+                              const VSrc &vs, const SeqGeom &g, int32_t nrows, int32_t renorm,
                               float *o, void *ws, const VtWs &w) {
   const int nbw = (g.maxnb + 31) / 32 > 0 ? (g.maxnb + 31) / 32 : 1;
   const size_t smem = apply_smem(B, map->num_heads, nbw);
@@ -1016,15 +1079,79 @@ static mf_status launch_apply(hipStream_t s, const mf_bsr_map *map, const float 
   const size_t vbufs = 2 * (size_t)B * D * 2;  // the two static V tile buffers of k_apply4
   const size_t vbufs_mix = (size_t)ApplyMixCfg<B, D, MF_TILE_BF16>::G * B * D * 2;
   if (smem + vbufs > 160 * 1024 || smem_mix + vbufs_mix > 160 * 1024) return MF_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL((k_vtranspose<B, D>), dim3(g.NBR, Hkv), dim3(256), 0, s,
-                     reinterpret_cast<const uint16_t *>(v), g.T, at<RowInfo>(ws, w.rt.rows), g.NBR,
-                     at<uint16_t>(ws, w.vt));
+  hipLaunchKernelGGL((k_vtranspose<B, D>), dim3(g.NBR, vs.Hkv), dim3(256), 0, s, vs, g.T,
+                     at<RowInfo>(ws, w.rt.rows), g.NBR, at<uint16_t>(ws, w.vt));
   if (hip_status() != MF_OK) return MF_ERR_HIP;
+  const int32_t *sched = at<int32_t>(ws, w.rt.sched);
+  if (vs.window) {
+    if (nrows == 0) return MF_OK;
+    hipLaunchKernelGGL(k_window_sched, dim3(1), dim3(1024), 0, s, at<RowInfo>(ws, w.rt.rows),
+                       sched, g.NBR, B, vs.window, at<int32_t>(ws, w.wsched));
+    if (hip_status() != MF_OK) return MF_ERR_HIP;
+    sched = at<int32_t>(ws, w.wsched);
+  }
   if (map->tile_format == MF_TILE_MXFP8)
-    return launch_apply_fmt<B, D, MF_TILE_MXFP8>(s, map, W, Ht, Hkv, g, renorm, o, ws, w, nbw,
-                                                 smem, smem_mix, vbufs, vbufs_mix);
-  return launch_apply_fmt<B, D, MF_TILE_BF16>(s, map, W, Ht, Hkv, g, renorm, o, ws, w, nbw, smem,
-                                              smem_mix, vbufs, vbufs_mix);
+    return launch_apply_fmt<B, D, MF_TILE_MXFP8>(s, map, W, Ht, vs.Hkv, g, renorm, o, ws, w, sched,
+                                                 nrows, nbw, smem, smem_mix, vbufs, vbufs_mix);
+  return launch_apply_fmt<B, D, MF_TILE_BF16>(s, map, W, Ht, vs.Hkv, g, renorm, o, ws, w, sched,
+                                              nrows, nbw, smem, smem_mix, vbufs, vbufs_mix);
+}
+
+// Shared argument checks and dispatch of both apply entry points.
+static mf_status apply_common(void *stream, const mf_bsr_map *map, const float *W, int32_t Ht,
+                              VSrc vs, int32_t d, const int32_t *cu_host, const int32_t *cu_dev,
+                              int32_t nseq, const int32_t *window_host, int32_t renorm, float *o,
+                              void *ws, size_t ws_bytes) {
+  const int32_t Hkv = vs.Hkv;
+  if (!map || !cu_host || !cu_dev || Ht <= 0 || Hkv <= 0 || Ht % Hkv != 0)
+    return MF_ERR_INVALID_ARG;
+  if (!valid_block(map->block)) return MF_ERR_INVALID_ARG;
+  if (!valid_dim(d)) return MF_ERR_UNSUPPORTED;
+  if (map->num_heads <= 0 || !W || !valid_tile_format(map->tile_format)) return MF_ERR_INVALID_ARG;
+  SeqGeom g;
+  mf_status st = seq_geom(cu_host, nseq, map->block, &g);
+  if (st != MF_OK) return st;
+  if (g.NBR != map->num_block_rows || g.T != map->total_tokens) return MF_ERR_INVALID_ARG;
+  if ((int64_t)g.NBR * Ht > INT32_MAX / 2) return MF_ERR_UNSUPPORTED;
+  if (g.T > 0 && (!(vs.v || vs.pages) || !o || !map->row_ptr || !map->col_idx || !map->tiles ||
+                  !map->kept_mass))
+    return MF_ERR_INVALID_ARG;
+  const int B = map->block;
+  int64_t nrows = g.NBR;
+  if (vs.pages) {
+    if (vs.page_size <= 0 || vs.num_pages <= 0 || vs.max_pages <= 0 || !vs.table)
+      return MF_ERR_INVALID_ARG;
+    for (int32_t s = 0; s < nseq; ++s)
+      if ((int64_t)cu_host[s + 1] - cu_host[s] > (int64_t)vs.max_pages * vs.page_size)
+        return MF_ERR_INVALID_ARG;  // the table cannot cover the sequence
+  }
+  if (vs.window) {
+    if (!window_host) return MF_ERR_INVALID_ARG;
+    nrows = 0;
+    for (int32_t s = 0; s < nseq; ++s) {
+      const int32_t L = cu_host[s + 1] - cu_host[s];
+      const int32_t a = window_host[2 * s], b = window_host[2 * s + 1];
+      if (a < 0 || b < a || b > L) return MF_ERR_INVALID_ARG;
+      if (a == b) continue;  // nothing of this sequence in the chunk
+      if (a % B != 0 || (b % B != 0 && b != L)) return MF_ERR_INVALID_ARG;
+      nrows += ((int64_t)b + B - 1) / B - a / B;
+    }
+  }
+  const VtWs w = vt_ws(g, Hkv, B, d);
+  if (!ws || ws_bytes < w.total) return MF_ERR_WORKSPACE;
+  if (g.NBR == 0) return MF_OK;
+  void *wsa = reinterpret_cast<void *>((reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if ((st = launch_rowtable(s, cu_dev, g, B, wsa, w.rt)) != MF_OK) return st;
+  const int32_t nr = (int32_t)nrows;
+  if (B == 32)
+    return d == 64 ? launch_apply<32, 64>(s, map, W, Ht, vs, g, nr, renorm, o, wsa, w)
+                   : launch_apply<32, 128>(s, map, W, Ht, vs, g, nr, renorm, o, wsa, w);
+  if (B == 64)
+    return d == 64 ? launch_apply<64, 64>(s, map, W, Ht, vs, g, nr, renorm, o, wsa, w)
+                   : launch_apply<64, 128>(s, map, W, Ht, vs, g, nr, renorm, o, wsa, w);
+  return d == 64 ? launch_apply<128, 64>(s, map, W, Ht, vs, g, nr, renorm, o, wsa, w)
+                 : launch_apply<128, 128>(s, map, W, Ht, vs, g, nr, renorm, o, wsa, w);
 }
 
 }  // namespace mf
@@ -1043,31 +1170,22 @@ extern "C" mf_status mf_apply_translated(void *stream, const mf_bsr_map *map, co
                                          const int32_t *cu_host, const int32_t *cu_dev,
                                          int32_t nseq, int32_t renorm, float *o, void *ws,
                                          size_t ws_bytes) {
-  if (!map || !cu_host || !cu_dev || Ht <= 0 || Hkv <= 0 || Ht % Hkv != 0)
-    return MF_ERR_INVALID_ARG;
-  if (!valid_block(map->block)) return MF_ERR_INVALID_ARG;
-  if (!valid_dim(d)) return MF_ERR_UNSUPPORTED;
-  if (map->num_heads <= 0 || !W || !valid_tile_format(map->tile_format)) return MF_ERR_INVALID_ARG;
-  SeqGeom g;
-  mf_status st = seq_geom(cu_host, nseq, map->block, &g);
-  if (st != MF_OK) return st;
-  if (g.NBR != map->num_block_rows || g.T != map->total_tokens) return MF_ERR_INVALID_ARG;
-  if ((int64_t)g.NBR * Ht > INT32_MAX / 2) return MF_ERR_UNSUPPORTED;
-  if (g.T > 0 && (!v || !o || !map->row_ptr || !map->col_idx || !map->tiles || !map->kept_mass))
-    return MF_ERR_INVALID_ARG;
-  const VtWs w = vt_ws(g, Hkv, map->block, d);
-  if (!ws || ws_bytes < w.total) return MF_ERR_WORKSPACE;
-  if (g.NBR == 0) return MF_OK;
-  void *wsa = reinterpret_cast<void *>((reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255));
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if ((st = launch_rowtable(s, cu_dev, g, map->block, wsa, w.rt)) != MF_OK) return st;
-  const int B = map->block;
-  if (B == 32)
-    return d == 64 ? launch_apply<32, 64>(s, map, W, Ht, v, Hkv, g, renorm, o, wsa, w)
-                   : launch_apply<32, 128>(s, map, W, Ht, v, Hkv, g, renorm, o, wsa, w);
-  if (B == 64)
-    return d == 64 ? launch_apply<64, 64>(s, map, W, Ht, v, Hkv, g, renorm, o, wsa, w)
-                   : launch_apply<64, 128>(s, map, W, Ht, v, Hkv, g, renorm, o, wsa, w);
-  return d == 64 ? launch_apply<128, 64>(s, map, W, Ht, v, Hkv, g, renorm, o, wsa, w)
-                 : launch_apply<128, 128>(s, map, W, Ht, v, Hkv, g, renorm, o, wsa, w);
+  VSrc vs{static_cast<const uint16_t *>(v), nullptr, nullptr, 0, 0, 0, Hkv, nullptr};
+  return apply_common(stream, map, W, Ht, vs, d, cu_host, cu_dev, nseq, nullptr, renorm, o, ws,
+                      ws_bytes);
+}
+
+extern "C" mf_status mf_apply_translated_paged(void *stream, const mf_bsr_map *map,
+                                               const float *W, int32_t Ht, const mf_paged_v *pv,
+                                               int32_t Hkv, int32_t d, const int32_t *cu_host,
+                                               const int32_t *cu_dev, int32_t nseq,
+                                               const int32_t *window_host,
+                                               const int32_t *window_dev, int32_t renorm,
+                                               float *o, void *ws, size_t ws_bytes) {
+  if (!pv || !pv->pages) return MF_ERR_INVALID_ARG;
+  if ((window_host == nullptr) != (window_dev == nullptr)) return MF_ERR_INVALID_ARG;
+  VSrc vs{nullptr, static_cast<const uint16_t *>(pv->pages), pv->block_table, pv->page_size,
+          pv->max_pages_per_seq, pv->num_pages, Hkv, window_dev};
+  return apply_common(stream, map, W, Ht, vs, d, cu_host, cu_dev, nseq, window_host, renorm, o,
+                      ws, ws_bytes);
 }

@@ -112,10 +112,11 @@ inline CompressWs compress_ws(const SeqGeom &g, int32_t Hs, int32_t B) {
   return w;
 }
 
-// Apply / dense workspace: row table + transposed, block-padded V.
+// Apply / dense workspace: row table + transposed, block-padded V + the
+// schedule of a query window.
 struct VtWs {
   RowTable rt;
-  size_t vt;
+  size_t vt, wsched;
   size_t total;
 };
 
@@ -124,6 +125,7 @@ inline VtWs vt_ws(const SeqGeom &g, int32_t Hkv, int32_t B, int32_t d) {
   VtWs w;
   w.rt = carve_rows(c, g);
   w.vt = c.take<uint16_t>((size_t)Hkv * d * (size_t)(g.NBR > 0 ? g.NBR : 1) * B);
+  w.wsched = c.take<int32_t>(g.NBR > 0 ? g.NBR : 1);
   w.total = c.off + 256;
   return w;
 }

@@ -26,7 +26,8 @@ EXPORTS = ("mf_num_block_rows", "mf_compress_max_tiles", "mf_compress_workspace_
            "mf_compress_topp", "mf_apply_workspace_bytes", "mf_apply_translated",
            "mf_dense_workspace_bytes", "mf_dense_ref_attention", "mf_read_status",
            "mf_status_string", "mf_prefix_dedupe_workspace_bytes", "mf_prefix_dedupe",
-           "mf_tile_bytes", "mf_tv_distance_workspace_bytes", "mf_tv_distance")
+           "mf_tile_bytes", "mf_tv_distance_workspace_bytes", "mf_tv_distance",
+           "mf_apply_translated_paged")
 
 
 class MfLogitBias(ctypes.Structure):
@@ -42,6 +43,11 @@ class MfBsrMap(ctypes.Structure):
                 ("kept_mass", ctypes.c_void_p), ("nnz", ctypes.c_void_p),
                 ("status", ctypes.c_void_p), ("row_alias", ctypes.c_void_p),
                 ("tile_format", ctypes.c_int32)]
+
+
+class MfPagedV(ctypes.Structure):
+    _fields_ = [("pages", ctypes.c_void_p), ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("block_table", ctypes.c_void_p), ("max_pages_per_seq", ctypes.c_int32)]
 
 
 class MapflowError(RuntimeError):
@@ -80,6 +86,8 @@ def load():
         "mf_prefix_dedupe_workspace_bytes": (sz, [pcu, i32, i32]),
         "mf_prefix_dedupe": (i32, [vp, vp, vp, i32, pcu, vp, i32, i32, i32, i32, vp, vp, sz]),
         "mf_tile_bytes": (i64, [i32, i32]),
+        "mf_apply_translated_paged": (i32, [vp, ctypes.POINTER(MfBsrMap), vp, i32, ctypes.POINTER(MfPagedV),
+                                            i32, i32, pcu, vp, i32, pcu, vp, i32, vp, vp, sz]),
         "mf_tv_distance_workspace_bytes": (sz, [pcu, i32, i32]),
         "mf_tv_distance": (i32, [vp, ctypes.POINTER(MfBsrMap), vp, i32, vp, vp, i32, i32, i32, pcu,
                                  vp, i32, ctypes.POINTER(MfLogitBias), i32, vp, vp, sz]),
@@ -320,6 +328,48 @@ def mf_apply_translated(m: BsrMap, W: torch.Tensor, v: torch.Tensor, cu_seqlens,
                                  _cu_ptr(cu), cu_dev.data_ptr(), len(cu) - 1, int(bool(renorm)),
                                  out.data_ptr(), workspace.data_ptr(), workspace.numel())
     _check("mf_apply_translated", st)
+    return out
+
+
+def mf_apply_translated_paged(m: BsrMap, W: torch.Tensor, pages: torch.Tensor, block_table: torch.Tensor,
+                              cu_seqlens, window=None, renorm: bool = True,
+                              out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                              cu_dev: Optional[torch.Tensor] = None,
+                              window_dev: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Translated retrieval with V in a paged pool pages [num_pages, Hkv, page_size, d]
+    (bf16) addressed through block_table [nseq, max_pages] (int32), optionally only
+    for the query-token windows `window` ([nseq][2], a prefill chunk per sequence);
+    rows outside the windows of `out` are left as they are."""
+    lib = load()
+    cu = _cu_host(cu_seqlens)
+    Ht = W.shape[0]
+    npages, Hkv, P, d = pages.shape
+    if pages.dtype != torch.bfloat16 or not pages.is_contiguous():
+        raise ValueError("pages must be contiguous bfloat16 [num_pages, Hkv, page_size, d]")
+    if block_table.dtype != torch.int32 or not block_table.is_contiguous() or block_table.dim() != 2:
+        raise ValueError("block_table must be contiguous int32 [nseq, max_pages]")
+    if W.dtype != torch.float32 or not W.is_contiguous() or W.shape[1] != m.num_heads:
+        raise ValueError("W must be contiguous float32 [Ht, Hs]")
+    dev = pages.device
+    T = int(cu[-1])
+    if out is None:
+        out = torch.zeros((Ht, T, d), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(mf_apply_workspace_bytes(Hkv, cu, m.block, d), dtype=torch.uint8, device=dev)
+    if cu_dev is None:
+        cu_dev = _dev_cu(cu, dev)
+    wh = wd = None
+    if window is not None:
+        wh = np.ascontiguousarray(np.asarray(window, dtype=np.int32).reshape(-1))
+        wd = window_dev if window_dev is not None else torch.from_numpy(wh).to(dev)
+    pv = MfPagedV(pages.data_ptr(), P, npages, block_table.data_ptr(), int(block_table.shape[1]))
+    cs = m.cstruct()
+    st = lib.mf_apply_translated_paged(_stream(), ctypes.byref(cs), W.data_ptr(), Ht, ctypes.byref(pv),
+                                       Hkv, d, _cu_ptr(cu), cu_dev.data_ptr(), len(cu) - 1,
+                                       _cu_ptr(wh) if wh is not None else None,
+                                       wd.data_ptr() if wd is not None else None, int(bool(renorm)),
+                                       out.data_ptr(), workspace.data_ptr(), workspace.numel())
+    _check("mf_apply_translated_paged", st)
     return out
 
 

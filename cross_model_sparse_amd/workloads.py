@@ -216,3 +216,28 @@ def receiver_qk(wl: Workload, Hkr: Optional[int] = None, alpha: float = 0.9,
         qb, kb = f32_to_bf16_bits(q), f32_to_bf16_bits(k)
         return bf16_bits_to_f32(qb), bf16_bits_to_f32(kb), qb, kb
     return q, k, None, None
+
+
+def paged_v(v_bits: np.ndarray, cu: np.ndarray, page_size: int, seed: int = 0, spare: int = 3):
+    """V [Hkv][T][d] (bf16 bits) laid out in a paged pool for retrieval with a page
+    table: every sequence's pages go to seeded random physical slots of a pool
+    [num_pages][Hkv][page_size][d] with `spare` unused pages; slots past a
+    sequence's end hold random bits.  Returns (pool, block_table [nseq][max_pages])."""
+    rng = np.random.default_rng(seed + 104729)
+    Hkv, T, d = v_bits.shape
+    lens = [int(b - a) for a, b in zip(cu[:-1], cu[1:])]
+    npg = [(L + page_size - 1) // page_size for L in lens]
+    maxp = max(npg + [1])
+    total = sum(npg) + spare
+    perm = rng.permutation(total)
+    pool = rng.integers(0, 1 << 16, size=(total, Hkv, page_size, d), dtype=np.uint16)
+    table = np.full((len(lens), maxp), -1, dtype=np.int32)
+    k = 0
+    for s, (a, L) in enumerate(zip(cu[:-1], lens)):
+        for p in range(npg[s]):
+            phys = int(perm[k])
+            k += 1
+            table[s, p] = phys
+            n = min(page_size, L - p * page_size)
+            pool[phys, :, :n, :] = v_bits[:, a + p * page_size:a + p * page_size + n, :]
+    return pool, table

@@ -228,8 +228,9 @@ mf_status mf_prefix_dedupe(void *stream, const void *q, const void *k, mf_dtype 
                            int32_t nseq, int32_t Hs, int32_t d, int32_t B, int32_t *row_alias,
                            void *workspace, size_t workspace_bytes);
 
-/* Device workspace bytes mf_apply_translated needs: a block-padded, transposed
- * copy of V ([Hkv][d][NBR * B] bf16) plus the block-row table.  0 if invalid. */
+/* Device workspace bytes mf_apply_translated and mf_apply_translated_paged need:
+ * a block-padded, transposed copy of V ([Hkv][d][NBR * B] bf16), the block-row
+ * table and a window schedule.  0 if invalid. */
 size_t mf_apply_workspace_bytes(int32_t Hkv, const int32_t *cu_seqlens_host, int32_t nseq,
                                 int32_t B, int32_t d);
 
@@ -254,6 +255,41 @@ mf_status mf_apply_translated(void *stream, const mf_bsr_map *map, const float *
                               const int32_t *cu_seqlens_host, const int32_t *cu_seqlens_dev,
                               int32_t nseq, int32_t renorm, float *o, void *workspace,
                               size_t workspace_bytes);
+
+/* V held in a paged cache (PagedAttention-style): token j of sequence s is at
+ * slot j % page_size of page block_table[s * max_pages_per_seq + j / page_size]
+ * in the pool.  Page indices outside [0, num_pages) read as zeros. */
+typedef struct mf_paged_v {
+  const void *pages;           /* [num_pages][Hkv][page_size][d] bf16, device    */
+  int32_t page_size;           /* tokens per page, >= 1                          */
+  int32_t num_pages;           /* pages in the pool                              */
+  const int32_t *block_table;  /* [nseq][max_pages_per_seq] int32, device        */
+  int32_t max_pages_per_seq;   /* must cover every sequence: L_s <= max * size   */
+} mf_paged_v;
+
+/* Translated retrieval with paged V and, optionally, chunked prefill (MapFlow §6:
+ * the fused kernel supports PagedAttention, chunked prefill and packed
+ * variable-length sequences).  Same computation as mf_apply_translated, with:
+ *
+ * pv          V through a page table (see mf_paged_v); host struct.
+ * window      NULL for whole sequences, or [nseq][2] int32 query-token windows
+ *             [begin, end) per sequence (a prefill chunk), given twice (host
+ *             copy for validation and sizing, device copy for the kernels).
+ *             begin must be a multiple of map->block; end a multiple of it or
+ *             the sequence length; an empty window (begin == end, anywhere in
+ *             [0, L]) skips the sequence.  Only output
+ *             rows inside the windows are written (o's other rows are left as
+ *             they are), and only V of keys before each window's end is read:
+ *             a chunk attends, through the map's rows of its own query blocks,
+ *             to every earlier chunk's keys and to its own.
+ * workspace   at least mf_apply_workspace_bytes(...) bytes.
+ * Errors: MF_ERR_INVALID_ARG, MF_ERR_UNSUPPORTED, MF_ERR_WORKSPACE, MF_ERR_HIP. */
+mf_status mf_apply_translated_paged(void *stream, const mf_bsr_map *map, const float *W,
+                                    int32_t Ht, const mf_paged_v *pv, int32_t Hkv, int32_t d,
+                                    const int32_t *cu_seqlens_host, const int32_t *cu_seqlens_dev,
+                                    int32_t nseq, const int32_t *window_host,
+                                    const int32_t *window_dev, int32_t renorm, float *o,
+                                    void *workspace, size_t workspace_bytes);
 
 /* Device workspace bytes mf_dense_ref_attention needs (transposed, block-padded
  * V, as for apply, with B = 64).  0 if invalid. */

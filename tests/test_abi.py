@@ -30,7 +30,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = header_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(mf.EXPORTS) == names
@@ -157,6 +157,54 @@ def test_tv_distance_rejects_bad_arguments(lib):
     assert f(*args(ws=need - 1)) == mf.MF_ERR_WORKSPACE
     m.num_block_rows = 5
     assert f(*args()) == mf.MF_ERR_INVALID_ARG
+
+
+def test_paged_v_layout_round_trip():
+    """The paged pool holds every token of every sequence at the slot its table says."""
+    rng = np.random.default_rng(1)
+    lens = [37, 0, 100, 16]
+    c = cu(lens)
+    v = rng.integers(0, 1 << 16, size=(3, int(c[-1]), 8), dtype=np.uint16)
+    for P in (1, 7, 16, 64):
+        pool, table = wlmod.paged_v(v, c, P, seed=P)
+        for s, L in enumerate(lens):
+            for j in range(L):
+                pg = table[s, j // P]
+                assert np.array_equal(pool[pg, :, j % P, :], v[:, c[s] + j, :])
+        used = table[table >= 0]
+        assert len(set(used.tolist())) == len(used) and used.max() < pool.shape[0]
+
+
+def test_apply_paged_rejects_bad_arguments(lib):
+    c = cu([100, 60])
+    fake = ctypes.c_void_p(16)
+    pc = c.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    m = mf.MfBsrMap(2, 32, 6, 160, 10, 8, 8, 8, 8, 8, 8, None, 0)
+    f = lib.mf_apply_translated_paged
+    ws = 1 << 40
+
+    def call(pv, win=None, wdev=fake):
+        wp = None
+        if win is not None:
+            arr = np.asarray(win, dtype=np.int32)
+            call.keep = arr
+            wp = arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+        else:
+            wdev = None
+        return f(None, ctypes.byref(m), fake, 4, ctypes.byref(pv) if pv is not None else None, 2, 64, pc,
+                 fake, 2, wp, wdev, 1, fake, fake, ws)
+
+    good = mf.MfPagedV(16, 16, 20, 16, 8)
+    assert call(None) == mf.MF_ERR_INVALID_ARG
+    assert call(mf.MfPagedV(None, 16, 20, 16, 8)) == mf.MF_ERR_INVALID_ARG
+    assert call(mf.MfPagedV(16, 0, 20, 16, 8)) == mf.MF_ERR_INVALID_ARG
+    assert call(mf.MfPagedV(16, 16, 20, 16, 6)) == mf.MF_ERR_INVALID_ARG   # 100 > 6 * 16
+    assert call(mf.MfPagedV(16, 16, 20, None, 8)) == mf.MF_ERR_INVALID_ARG
+    assert call(good, [[0, 64], [32, 60]], None) == mf.MF_ERR_INVALID_ARG  # host without device copy
+    assert call(good, [[16, 64], [0, 60]]) == mf.MF_ERR_INVALID_ARG         # begin not block-aligned
+    assert call(good, [[0, 50], [0, 60]]) == mf.MF_ERR_INVALID_ARG          # end mid-block, not L
+    assert call(good, [[0, 128], [0, 60]]) == mf.MF_ERR_INVALID_ARG         # end past L
+    assert call(good, [[64, 32], [0, 60]]) == mf.MF_ERR_INVALID_ARG         # end before begin
 
 
 def test_status_strings(lib):

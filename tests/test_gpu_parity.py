@@ -510,3 +510,88 @@ def test_tv_self_is_one_minus_kept_mass_full_size(gpu, fmt):
     tol = 2.0 ** -9 + 2e-5 if fmt == "bf16" else 2.0 ** -5 + 2e-5
     say(f"full workload 4 tv {fmt}: mean tv {float(tv.mean()):.4f}, max |tv - (1 - kmass)| {float(e.max()):.2e}")
     assert float(e.max()) <= tol
+
+
+# ---------------------------------------------------------------------------
+# paged V and chunked prefill
+# ---------------------------------------------------------------------------
+
+def _pages_dev(wl, P, dev, seed=0):
+    pool, table = wlmod.paged_v(wl.v_bits, wl.cu_seqlens, P, seed=seed)
+    return (torch.from_numpy(pool.view(np.int16)).to(dev).view(torch.bfloat16),
+            torch.from_numpy(table).to(dev))
+
+
+def _chunks(lens, B, blocks_per_chunk):
+    """Per call, one query window per sequence: chunk c covers blocks
+    [c * n, (c + 1) * n) (clipped to the sequence), empty once a sequence is done."""
+    ncalls = max((((L + B - 1) // B) + blocks_per_chunk - 1) // blocks_per_chunk for L in lens)
+    out = []
+    for c in range(ncalls):
+        w = []
+        for L in lens:
+            a = min(c * blocks_per_chunk * B, L)
+            b = min((c + 1) * blocks_per_chunk * B, L)
+            w.append([a, b])
+        out.append(w)
+    return out
+
+
+@pytest.mark.parametrize("idx,lens,kw,P,fmt", [
+    (5, [300, 520, 64, 1, 129, 0, 700], dict(Hs=4, Ht=4, Hkv=4), 16, "bf16"),
+    (3, [777], dict(Hs=6, Ht=8, Hkv=2), 7, "bf16"),
+    (4, [1100, 333], dict(Hs=8, Ht=16, Hkv=16), 128, "mxfp8"),
+])
+def test_paged_chunked_equals_plain(gpu, idx, lens, kw, P, fmt):
+    """Paged V gives bitwise the plain output; chunked calls write only their own
+    rows (the rest keeps a sentinel) and together give bitwise the plain output;
+    one chunk against the oracle directly."""
+    wl = wlmod.small_variant(idx, lens, **kw)
+    B = wl.spec.B
+    m, st, nnz = gpu_compress(wl, gpu, tile_format=fmt)
+    assert st == mf.MF_OK
+    Wt = torch.from_numpy(np.ascontiguousarray(wl.W)).to(gpu)
+    O0 = mf.mf_apply_translated(m, Wt, to_dev_v(wl, gpu), wl.cu_seqlens)
+    pool, table = _pages_dev(wl, P, gpu, seed=P)
+    O1 = mf.mf_apply_translated_paged(m, Wt, pool, table, wl.cu_seqlens)
+    assert torch.equal(O0, O1), "paged V differs from contiguous V"
+    sentinel = 12345.0
+    O2 = torch.full_like(O0, sentinel)
+    chunks = _chunks(wl.lens, B, 3)
+    for c, win in enumerate(chunks):
+        mf.mf_apply_translated_paged(m, Wt, pool, table, wl.cu_seqlens, window=win, out=O2)
+        if c == 0:
+            done = torch.zeros(wl.T, dtype=torch.bool)
+            for s, (a, b) in enumerate(win):
+                done[int(wl.cu_seqlens[s]) + a:int(wl.cu_seqlens[s]) + b] = True
+            Oc = O2.cpu()
+            assert torch.all(Oc[:, ~done] == sentinel), "a chunk wrote rows outside its window"
+            assert torch.equal(Oc[:, done], O0.cpu()[:, done])
+    assert torch.equal(O0, O2), "chunked calls differ from the whole-sequence call"
+    # the second chunk against the oracle
+    win = chunks[min(1, len(chunks) - 1)]
+    rows = [(s, I) for s, (a, b) in enumerate(win) for I in range(a // B, (b + B - 1) // B)]
+    res = orc.compress(wl.q, wl.k, wl.cu_seqlens, B, wl.spec.p, wl.bias(), rows=rows)
+    out = orc.apply(res, wl.W, wl.v, wl.cu_seqlens, B, wl.spec.Hkv, rows=rows,
+                    codec="mxfp8" if fmt == "mxfp8" else None)
+    hm = HostMap(m, rows=[h * m.num_block_rows + global_row(wl.cu_seqlens, B, s, I)
+                          for h in range(wl.spec.Hs) for (s, I) in rows])
+    stats = check_rows(hm, res, wl.cu_seqlens, wl.T)
+    err = check_apply(O2.cpu().numpy(), out, wl.cu_seqlens, B, {(s, I) for (h, s, I) in stats["flips"]})
+    say(f"paged P={P} {fmt}: {len(chunks)} chunks, rows {len(rows)} of chunk 1 vs oracle {err:.2e}")
+
+
+def test_paged_chunked_full_size(gpu):
+    """Long-context workload at full size: V in 16-token pages, prefill in four
+    8192-token chunks; the chunks together equal the plain call bit for bit."""
+    wl = wlmod.make_config(4)
+    B = wl.spec.B
+    m, st, nnz = gpu_compress(wl, gpu)
+    assert st == mf.MF_OK
+    Wt = torch.from_numpy(wl.W).to(gpu)
+    O0 = mf.mf_apply_translated(m, Wt, to_dev_v(wl, gpu), wl.cu_seqlens)
+    pool, table = _pages_dev(wl, 16, gpu)
+    O2 = torch.empty_like(O0)
+    for win in _chunks(wl.lens, B, 64):
+        mf.mf_apply_translated_paged(m, Wt, pool, table, wl.cu_seqlens, window=win, out=O2)
+    assert torch.equal(O0, O2)
