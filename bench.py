@@ -188,6 +188,10 @@ def main():
     ap.add_argument("--tv", action="store_true",
                     help="time mf_tv_distance (translated map vs a synthetic receiver's own map) "
                          "on the compressed map instead of the compress + apply step")
+    ap.add_argument("--paged", type=int, default=0, metavar="P",
+                    help="V in a paged pool of P-token pages (mf_apply_translated_paged)")
+    ap.add_argument("--chunks", type=int, default=1,
+                    help="with --paged: prefill in this many query chunks per step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (HBM counter scale)")
     args = ap.parse_args()
@@ -239,9 +243,31 @@ def main():
         mf.mf_compress_topp(q, k, cu, s.B, s.p, bias, out=m, workspace=ws_c, cu_dev=cu_dev,
                             row_alias=ra)
 
+    windows = None
+    if args.paged:
+        pool_np, table_np = wlmod.paged_v(wl.v_bits, cu, args.paged)
+        pool = torch.from_numpy(pool_np.view(np.int16)).to(dev).view(torch.bfloat16)
+        table = torch.from_numpy(table_np).to(dev)
+        del pool_np
+        nbmax = max((L + s.B - 1) // s.B for L in wl.lens)
+        per = (nbmax + args.chunks - 1) // args.chunks
+        windows = []
+        for c in range(args.chunks):
+            w = [[min(c * per * s.B, L), min((c + 1) * per * s.B, L)] for L in wl.lens]
+            windows.append((w, torch.from_numpy(np.asarray(w, dtype=np.int32).reshape(-1)).to(dev)))
+
+    def apply():
+        if args.paged:
+            for w, wd in windows:
+                mf.mf_apply_translated_paged(m, W, pool, table, cu, window=w if args.chunks > 1 else None,
+                                             out=O, workspace=ws_a, cu_dev=cu_dev,
+                                             window_dev=wd if args.chunks > 1 else None)
+        else:
+            mf.mf_apply_translated(m, W, v, cu, out=O, workspace=ws_a, cu_dev=cu_dev)
+
     def step():
         compress()
-        mf.mf_apply_translated(m, W, v, cu, out=O, workspace=ws_a, cu_dev=cu_dev)
+        apply()
 
     for _ in range(args.warmup):
         step()
@@ -267,7 +293,7 @@ def main():
         ev[i][0].record(stream)
         compress()
         ev[i][1].record(stream)
-        mf.mf_apply_translated(m, W, v, cu, out=O, workspace=ws_a, cu_dev=cu_dev)
+        apply()
         ev[i][2].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -283,6 +309,8 @@ def main():
     ab = algorithmic_bytes(wl, nnz, args.tile_format)
     fl = mfma_flops(torch, wl, m, W, nnz)
     workload = f"workload{args.config}" + ("" if args.tile_format == "bf16" else f"_{args.tile_format}")
+    if args.paged:
+        workload += f"_paged{args.paged}x{args.chunks}"
     achieved = ab["apply"] / (t_apply * 1e-3) / 1e9
     traffic = traffic_record("mf_apply_translated", workload)
     roof = dict(kernel="mf_apply_translated (fused retrieval)", bound="hbm", achieved=round(achieved, 1),
@@ -309,7 +337,7 @@ def main():
         log(f"dedupe: {shared} of {len(a)} block-rows share an earlier one")
     line = {
         "metric": ("compressed-map prefill tokens/s at L=32K (compress+apply)"
-                   if args.config == 4 and args.tile_format == "bf16"
+                   if args.config == 4 and args.tile_format == "bf16" and not args.paged
                    else "compressed-map prefill tokens/s (compress+apply)"),
         "value": round(wl.T / (ms_step * 1e-3), 1),
         "unit": "tokens/s",
@@ -325,6 +353,7 @@ def main():
         "config": {"workload": s.name, "tokens": wl.T, "source_heads": s.Hs, "target_heads": s.Ht,
                    "v_heads": s.Hkv, "head_dim": s.d, "block": s.B, "top_p": s.p,
                    "kept_tiles": nnz, "tile_format": args.tile_format,
+                   "v_pages": args.paged or None, "prefill_chunks": args.chunks if args.paged else 1,
                    "prefix_dedupe": bool(args.dedupe),
                    "parallelism": "none (1 GPU)"},
         "roofline": roof,
