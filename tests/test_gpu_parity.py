@@ -595,3 +595,56 @@ def test_paged_chunked_full_size(gpu):
     for win in _chunks(wl.lens, B, 64):
         mf.mf_apply_translated_paged(m, Wt, pool, table, wl.cu_seqlens, window=win, out=O2)
     assert torch.equal(O0, O2)
+
+
+# ---------------------------------------------------------------------------
+# feature combinations
+# ---------------------------------------------------------------------------
+
+def test_fp8_capacity_overflow_reported_and_bounded(gpu):
+    """An fp8 map with too little capacity reports it and writes no tile (codes or
+    scale bytes) and no index past its capacity."""
+    wl = wlmod.small_variant(4, [600], Hs=4, Ht=8, Hkv=8)
+    B = wl.spec.B
+    m0, st0, nnz = gpu_compress(wl, gpu, tile_format="mxfp8")
+    assert st0 == mf.MF_OK
+    cap = nnz // 2
+    big = mf.alloc_map(wl.spec.Hs, wl.cu_seqlens, B, gpu, capacity=cap + 16, tile_format="mxfp8")
+    big.tiles[cap:] = 0xA5
+    big.col_idx[cap:] = -77
+    m = mf.BsrMap(big.num_heads, B, big.num_block_rows, big.total_tokens, big.row_ptr,
+                  big.col_idx[:cap], big.tiles, big.kept_mass, big.nnz, big.status, tile_format="mxfp8")
+    q, k = to_dev_qk(wl, gpu)
+    mf.mf_compress_topp(q, k, wl.cu_seqlens, B, wl.spec.p, wl.bias(), out=m)
+    st, nnz2 = mf.mf_read_status(m)
+    assert st == mf.MF_ERR_CAPACITY and nnz2 == nnz
+    assert bool(torch.all(big.tiles[cap:] == 0xA5))
+    assert int((big.col_idx[cap:] != -77).sum()) == 0
+    assert torch.equal(big.tiles[:cap], m0.tiles[:cap])
+
+
+def test_tv_and_paged_on_shared_prefix_maps(gpu):
+    """A map with shared block-rows (prefix dedupe) gives bitwise the same TV
+    distances and, through the paged chunked path, the same outputs as the plain
+    map; with fp8 tiles too."""
+    wl = _multiturn([600, 1000, 130, 900, 420], Hs=4, Ht=6, Hkv=3)
+    B = wl.spec.B
+    q, k = to_dev_qk(wl, gpu)
+    alias = mf.mf_prefix_dedupe(q, k, wl.cu_seqlens, B)
+    Wt, vd = torch.from_numpy(wl.W).to(gpu), to_dev_v(wl, gpu)
+    rq, rk, rqb, rkb = wlmod.receiver_qk(wl, 3)
+    qd, kd = _receiver_dev(rq, rk, rqb, rkb, gpu)
+    pool, table = _pages_dev(wl, 32, gpu)
+    for fmt in ("bf16", "mxfp8"):
+        m0 = mf.mf_compress_topp(q, k, wl.cu_seqlens, B, wl.spec.p, wl.bias(), tile_format=fmt)
+        m1 = mf.mf_compress_topp(q, k, wl.cu_seqlens, B, wl.spec.p, wl.bias(), row_alias=alias,
+                                 tile_format=fmt)
+        assert mf.mf_read_status(m0)[0] == mf.MF_OK and mf.mf_read_status(m1)[0] == mf.MF_OK
+        tv0 = mf.mf_tv_distance(m0, Wt, qd, kd, wl.cu_seqlens, wl.bias())
+        tv1 = mf.mf_tv_distance(m1, Wt, qd, kd, wl.cu_seqlens, wl.bias())
+        assert torch.equal(tv0, tv1), fmt
+        O0 = mf.mf_apply_translated(m0, Wt, vd, wl.cu_seqlens)
+        O1 = torch.zeros_like(O0)
+        for win in _chunks(wl.lens, B, 5):
+            mf.mf_apply_translated_paged(m1, Wt, pool, table, wl.cu_seqlens, window=win, out=O1)
+        assert torch.equal(O0, O1), fmt
