@@ -899,22 +899,23 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(2))) void
                                  col0, wave, lane);
 
     u32x4 amix[G];
+    // Buffer loads through one descriptor per source (wave-uniform base, 32-bit
+    // lane offsets), zero-length for a source without a tile at this block, so
+    // missing tiles read as zeros with no branch and no 64-bit lane addresses.
     auto load_batch = [&](u32x4 (&d)[SB], uint32_t (&sb)[SB], int kc, int u0) {
 #pragma unroll
       for (int e = 0; e < SB; ++e) {
         const int t_ = tile_at(u0 + e);
-        d[e] = u32x4{0u, 0u, 0u, 0u};
-        sb[e] = 0u;
-        if (t_ >= 0) {
-          const char *tp = tiles + (int64_t)t_ * C::TBYTES;
-          if constexpr (!FP8) {
-            d[e] = *reinterpret_cast<const u32x4 *>(tp + loff + kc * 1024);
-          } else {
-            const u32x2 c2 =
-                *reinterpret_cast<const u32x2 *>(tp + loff + (kc / NP) * 512 * NP + (kc % NP) * 8);
-            d[e] = u32x4{c2[0], c2[1], 0u, 0u};
-            sb[e] = *reinterpret_cast<const uint8_t *>(tp + soff + kc);
-          }
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(tiles + (int64_t)(t_ >= 0 ? t_ : 0) * C::TBYTES), 0,
+            t_ >= 0 ? (int)C::TBYTES : 0, kBufferFlags);
+        if constexpr (!FP8) {
+          d[e] = __builtin_amdgcn_raw_buffer_load_b128(r, loff, kc * 1024, 0);
+          sb[e] = 0u;
+        } else {
+          const auto c2 = __builtin_amdgcn_raw_buffer_load_b64(r, loff, (kc / NP) * 512 * NP + (kc % NP) * 8, 0);
+          d[e] = u32x4{c2[0], c2[1], 0u, 0u};
+          sb[e] = __builtin_amdgcn_raw_buffer_load_b8(r, soff, kc, 0);
         }
       }
     };
