@@ -182,44 +182,39 @@ __attribute__((amdgpu_waves_per_eu((F32 || B + D >= 192) ? 1 : 2))) void k_tv(
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int q = q0 + u;
-      const char *tp = nullptr;
+      int64_t ti = -1;
       if (q < ns) {
         const uint32_t word = __builtin_amdgcn_readfirstlane(bm[q * nbw + (J >> 5)]);
         if ((word >> (J & 31)) & 1u) {
-          const int64_t ti = rbase[q] + pc[q * nbw + (J >> 5)] + __popc(word & ((1u << (J & 31)) - 1u));
-          if (ti < capacity) tp = tiles + ti * TBYTES;
+          const int64_t x = rbase[q] + pc[q * nbw + (J >> 5)] + __popc(word & ((1u << (J & 31)) - 1u));
+          if (x < capacity) ti = x;
         }
       }
-      float c = 0.f;
-      if (tp) c = coef[q * B + i_loc];
+      // one descriptor per source, zero-length without a tile: absent tiles
+      // read as zeros with no branch and no 64-bit lane addresses
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)(tiles + (ti >= 0 ? ti : 0) * TBYTES), 0, ti >= 0 ? (int)TBYTES : 0, 0x00020000);
+      cq[u] = ti >= 0 ? coef[q * B + i_loc] : 0.f;
 #pragma unroll
-      for (int mb = 0; mb < B / 32; ++mb) {
+      for (int mb = 0; mb < B / 32; ++mb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           if constexpr (!FP8) {
-            raw[u][mb][g] = tp ? *reinterpret_cast<const uint2 *>(
-                                     tp + (((i_loc >> 4) * (B / 32) + mb) * 64 + g * 16 + (i_loc & 15)) * 16 + 8 * hl)
-                               : uint2{0u, 0u};
+            const auto w2 = __builtin_amdgcn_raw_buffer_load_b64(
+                r, (((i_loc >> 4) * (B / 32) + mb) * 64 + g * 16 + (i_loc & 15)) * 16 + 8 * hl, 0, 0);
+            raw[u][mb][g] = uint2{w2[0], w2[1]};
           } else {
-            raw[u][mb][g] = tp ? *reinterpret_cast<const uint32_t *>(
-                                     tp + (((i_loc >> 4) * (B / (32 * NP)) + mb / NP) * 64 + g * 16 + (i_loc & 15)) * 8 * NP +
-                                     (mb % NP) * 8 + 4 * hl)
-                               : 0u;
+            raw[u][mb][g] = __builtin_amdgcn_raw_buffer_load_b32(
+                r, (((i_loc >> 4) * (B / (32 * NP)) + mb / NP) * 64 + g * 16 + (i_loc & 15)) * 8 * NP +
+                       (mb % NP) * 8 + 4 * hl, 0, 0);
           }
         }
-      }
       if constexpr (FP8) {
-        // the row's B/32 scale bytes in one word (zero for a missing tile)
-        uint32_t sw = 0u;
-        if (tp) {
-          const char *sp = tp + B * B + i_loc * (B / 32);
-          if constexpr (B == 128) sw = *reinterpret_cast<const uint32_t *>(sp);
-          else if constexpr (B == 64) sw = *reinterpret_cast<const uint16_t *>(sp);
-          else sw = *reinterpret_cast<const uint8_t *>(sp);
-        }
-        raw_scale[u] = sw;
+        // the row's B/32 scale bytes in one word
+        if constexpr (B == 128) raw_scale[u] = __builtin_amdgcn_raw_buffer_load_b32(r, i_loc * 4, B * B, 0);
+        else if constexpr (B == 64) raw_scale[u] = __builtin_amdgcn_raw_buffer_load_b16(r, i_loc * 2, B * B, 0);
+        else raw_scale[u] = __builtin_amdgcn_raw_buffer_load_b8(r, i_loc, B * B, 0);
       }
-      cq[u] = c;
     }
   };
   auto mix_group = [&](f32x16 (&mix)[B / 32], int q0) {
