@@ -178,6 +178,8 @@ __attribute__((amdgpu_waves_per_eu((F32 || B + D >= 192) ? 1 : 2))) void k_tv(
   Raw raw[4][B / 32][4];
   uint32_t raw_scale[4];
   float cq[4];
+  const int voff = FP8 ? ((i_loc >> 4) * (B / (32 * NP)) * 64 + (i_loc & 15)) * 8 * NP + 4 * hl
+                       : ((i_loc >> 4) * (B / 32) * 64 + (i_loc & 15)) * 16 + 8 * hl;
   auto load_group = [&](int q0, int J) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -195,18 +197,18 @@ __attribute__((amdgpu_waves_per_eu((F32 || B + D >= 192) ? 1 : 2))) void k_tv(
       const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
           (void *)(tiles + (ti >= 0 ? ti : 0) * TBYTES), 0, ti >= 0 ? (int)TBYTES : 0, 0x00020000);
       cq[u] = ti >= 0 ? coef[q * B + i_loc] : 0.f;
+      // per-lane part of the offset in one register, the (mb, g) part a
+      // constant scalar offset, so one lane offset serves all 16 loads
 #pragma unroll
       for (int mb = 0; mb < B / 32; ++mb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           if constexpr (!FP8) {
-            const auto w2 = __builtin_amdgcn_raw_buffer_load_b64(
-                r, (((i_loc >> 4) * (B / 32) + mb) * 64 + g * 16 + (i_loc & 15)) * 16 + 8 * hl, 0, 0);
+            const auto w2 = __builtin_amdgcn_raw_buffer_load_b64(r, voff, (mb * 64 + g * 16) * 16, 0);
             raw[u][mb][g] = uint2{w2[0], w2[1]};
           } else {
             raw[u][mb][g] = __builtin_amdgcn_raw_buffer_load_b32(
-                r, (((i_loc >> 4) * (B / (32 * NP)) + mb / NP) * 64 + g * 16 + (i_loc & 15)) * 8 * NP +
-                       (mb % NP) * 8 + 4 * hl, 0, 0);
+                r, voff, ((mb / NP) * 64 + g * 16) * 8 * NP + (mb % NP) * 8, 0);
           }
         }
       if constexpr (FP8) {
