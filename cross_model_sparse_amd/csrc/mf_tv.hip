@@ -30,13 +30,20 @@ inline size_t tv_smem(int B, int Hs, int nbw) {
   return (size_t)Hs * (8 + 4) + (size_t)Hs * nbw * 8 + (size_t)Hs * B * 4 + 64;
 }
 
-// Register budget: one wave per SIMD (the whole register file) wherever the
-// S^T tile, the 64 translated values and four sources' prefetched tile values
-// do not fit 256 VGPRs; at B = 128, d = 128 the LDS holds one work-group per CU
-// anyway.
+// Occupancy.  With bf16 Q/K and B <= 64 a work-group fits half a CU: one K
+// tile buffer (two barriers per block) and 256 VGPRs, so two waves share each
+// SIMD and hide each other's load latency; the sources' tile values load after
+// the block's probabilities.  Otherwise (B = 128, or fp32 Q/K) one wave per SIMD
+// holds the whole register file: two K tile buffers (one barrier per block),
+// and the first four sources' tile values load before the QK^T tile, so their
+// latency hides behind the MFMAs.  Either way the translated values are
+// subtracted from the receiver's probabilities in place.
+template <int B, int D, bool F32>
+constexpr bool tv_two_waves() { return !F32 && B <= 64; }
+
 template <int B, int D, bool F32, int FMT>
 __global__ __launch_bounds__(B * 2)
-__attribute__((amdgpu_waves_per_eu((F32 || B + D >= 192) ? 1 : 2))) void k_tv(
+__attribute__((amdgpu_waves_per_eu(tv_two_waves<B, D, F32>() ? 2 : 1))) void k_tv(
     const int64_t *__restrict__ row_ptr, const int32_t *__restrict__ col_idx,
     const char *__restrict__ tiles, const float *__restrict__ kept_mass, int32_t Hs, int32_t NBR,
     int64_t T, const float *__restrict__ W, int32_t Ht, int32_t grp, const void *__restrict__ qv,
@@ -48,7 +55,9 @@ __attribute__((amdgpu_waves_per_eu((F32 || B + D >= 192) ? 1 : 2))) void k_tv(
   constexpr bool FP8 = FMT == MF_TILE_MXFP8;
   constexpr int NP = (FP8 && B >= 64) ? 2 : 1;
   constexpr int64_t TBYTES = tile_bytes(B, FMT);
-  __shared__ __attribute__((aligned(16))) char kbuf[2 * C::KBYTES];
+  constexpr bool TW = tv_two_waves<B, D, F32>();
+  constexpr int NKB = TW ? 1 : 2;  // K tile buffers
+  __shared__ __attribute__((aligned(16))) char kbuf[NKB * C::KBYTES];
   extern __shared__ __attribute__((aligned(16))) char smem[];
   int64_t *rbase = reinterpret_cast<int64_t *>(smem);
   int32_t *src = reinterpret_cast<int32_t *>(smem + Hs * 8);
@@ -129,8 +138,13 @@ __attribute__((amdgpu_waves_per_eu((F32 || B + D >= 192) ? 1 : 2))) void k_tv(
   QOp<D, F32> qo;
   load_q<D>(qo, rvalid ? qh + (tok0 + i_pos) * D : nullptr, hl);
 
-  // K tiles alternate between two LDS buffers, one barrier per block
+  // Block J + 1 of K loads into registers while block J is multiplied.  Two
+  // buffers: it is stored into the other buffer, and one barrier per block
+  // makes it visible.  One buffer: a barrier (every wave's reads of block J
+  // done) comes first, and the barrier that ends the step makes it visible.
   u32x4 stg[C::NCH];
+  auto kcur_of = [&](int J) -> const char * { return kbuf + (NKB == 2 ? (J & 1) * C::KBYTES : 0); };
+  auto knext_of = [&](int J) -> char * { return kbuf + (NKB == 2 ? ((J + 1) & 1) * C::KBYTES : 0); };
   auto stage_first = [&]() {
     gload_tile<B, D, F32>(stg, kh, tok0, min(B, L), tid);
     lstore_tile<B, D, F32>(kbuf, stg, tid);
@@ -141,11 +155,13 @@ __attribute__((amdgpu_waves_per_eu((F32 || B + D >= 192) ? 1 : 2))) void k_tv(
   float lse_run = -INFINITY;
   stage_first();
   for (int J = 0; J <= I; ++J) {
-    const char *kcur = kbuf + (J & 1) * C::KBYTES;
-    char *knext = kbuf + ((J + 1) & 1) * C::KBYTES;
     if (J < I) gload_tile<B, D, F32>(stg, kh, tok0 + (int64_t)(J + 1) * B, min(B, L - (J + 1) * B), tid);
     f32x16 acc[B / 32];
-    st_tile<B, D>(acc, kcur, qo, lane);
+    st_tile<B, D>(acc, kcur_of(J), qo, lane);
+    if (NKB == 1 && J < I) {
+      __syncthreads();
+      lstore_tile<B, D, F32>(knext_of(J), stg, tid);
+    }
     float lse_t, off;
     if (uniform_tile(I, J, B, bias.sink_n, bias.sink2, bias.local_w, bias.local2, off)) {
       const float mr = pair_max(lane_rawmax<B>(acc));
@@ -164,7 +180,8 @@ __attribute__((amdgpu_waves_per_eu((F32 || B + D >= 192) ? 1 : 2))) void k_tv(
       const float mm = fmaxf(lse_run, lse_t);
       lse_run = mm + fast_log2(fast_exp2(lse_run - mm) + fast_exp2(lse_t - mm));
     }
-    if (J < I) lstore_tile<B, D, F32>(knext, stg, tid);
+    if (NKB == 2 && J < I) lstore_tile<B, D, F32>(knext_of(J), stg, tid);
+    // also after the last block: its reads done before pass 2 restages block 0
     __syncthreads();
   }
   // rows past the sequence end: -lse = -inf makes every probability exactly 0
@@ -219,33 +236,33 @@ __attribute__((amdgpu_waves_per_eu((F32 || B + D >= 192) ? 1 : 2))) void k_tv(
       }
     }
   };
-  auto mix_group = [&](f32x16 (&mix)[B / 32], int q0) {
-    (void)q0;
+  // the group's translated values, subtracted from the receiver's probabilities
+  auto sub_group = [&](f32x16 (&d)[B / 32]) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
 #pragma unroll
       for (int mb = 0; mb < B / 32; ++mb) {
         if constexpr (!FP8) {
-          const float c = cq[u];
+          const float c = -cq[u];
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const uint2 w2 = raw[u][mb][g];
-            mix[mb][4 * g + 0] = fmaf(c, bf16lo(w2.x), mix[mb][4 * g + 0]);
-            mix[mb][4 * g + 1] = fmaf(c, bf16hi(w2.x), mix[mb][4 * g + 1]);
-            mix[mb][4 * g + 2] = fmaf(c, bf16lo(w2.y), mix[mb][4 * g + 2]);
-            mix[mb][4 * g + 3] = fmaf(c, bf16hi(w2.y), mix[mb][4 * g + 3]);
+            d[mb][4 * g + 0] = fmaf(c, bf16lo(w2.x), d[mb][4 * g + 0]);
+            d[mb][4 * g + 1] = fmaf(c, bf16hi(w2.x), d[mb][4 * g + 1]);
+            d[mb][4 * g + 2] = fmaf(c, bf16lo(w2.y), d[mb][4 * g + 2]);
+            d[mb][4 * g + 3] = fmaf(c, bf16hi(w2.y), d[mb][4 * g + 3]);
           }
         } else {
           const int sb = (int)((raw_scale[u] >> (8 * mb)) & 0xffu);
-          const float cs = __builtin_amdgcn_ldexpf(cq[u], sb - 127);
+          const float cs = -__builtin_amdgcn_ldexpf(cq[u], sb - 127);
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(raw[u][mb][g], false);
             const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(raw[u][mb][g], true);
-            mix[mb][4 * g + 0] = fmaf(cs, lo[0], mix[mb][4 * g + 0]);
-            mix[mb][4 * g + 1] = fmaf(cs, lo[1], mix[mb][4 * g + 1]);
-            mix[mb][4 * g + 2] = fmaf(cs, hi[0], mix[mb][4 * g + 2]);
-            mix[mb][4 * g + 3] = fmaf(cs, hi[1], mix[mb][4 * g + 3]);
+            d[mb][4 * g + 0] = fmaf(cs, lo[0], d[mb][4 * g + 0]);
+            d[mb][4 * g + 1] = fmaf(cs, lo[1], d[mb][4 * g + 1]);
+            d[mb][4 * g + 2] = fmaf(cs, hi[0], d[mb][4 * g + 2]);
+            d[mb][4 * g + 3] = fmaf(cs, hi[1], d[mb][4 * g + 3]);
           }
         }
       }
@@ -254,13 +271,14 @@ __attribute__((amdgpu_waves_per_eu((F32 || B + D >= 192) ? 1 : 2))) void k_tv(
   float tvl = 0.f;
   stage_first();
   for (int J = 0; J <= I; ++J) {
-    const char *kcur = kbuf + (J & 1) * C::KBYTES;
-    char *knext = kbuf + ((J + 1) & 1) * C::KBYTES;
     if (J < I) gload_tile<B, D, F32>(stg, kh, tok0 + (int64_t)(J + 1) * B, min(B, L - (J + 1) * B), tid);
-    // the first four sources' tile values load while the QK^T tile is computed
-    load_group(0, J);
+    if (!TW) load_group(0, J);
     f32x16 acc[B / 32];
-    st_tile<B, D>(acc, kcur, qo, lane);
+    st_tile<B, D>(acc, kcur_of(J), qo, lane);
+    if (NKB == 1 && J < I) {
+      __syncthreads();
+      lstore_tile<B, D, F32>(knext_of(J), stg, tid);
+    }
     float off;
     if (uniform_tile(I, J, B, bias.sink_n, bias.sink2, bias.local_w, bias.local2, off)) {
       const float c0 = nlse2 + off;
@@ -276,20 +294,18 @@ __attribute__((amdgpu_waves_per_eu((F32 || B + D >= 192) ? 1 : 2))) void k_tv(
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[mb][r] = fast_exp2(acc[mb][r] + nlse2);
     }
-    // translated values of the lane's 64 elements, sources four at a time
-    f32x16 mix[B / 32];
-#pragma unroll
-    for (int mb = 0; mb < B / 32; ++mb) mix[mb] = zero16();
+    // receiver minus translated values of the lane's 64 elements, sources four
+    // at a time
     for (int q0 = 0; q0 < ns; q0 += 4) {
-      if (q0 > 0) load_group(q0, J);
-      mix_group(mix, q0);
+      if (TW || q0 > 0) load_group(q0, J);
+      sub_group(acc);
     }
 #pragma unroll
     for (int mb = 0; mb < B / 32; ++mb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) tvl += fabsf(mix[mb][r] - acc[mb][r]);
-    if (J < I) lstore_tile<B, D, F32>(knext, stg, tid);
-    __syncthreads();
+      for (int r = 0; r < 16; ++r) tvl += fabsf(acc[mb][r]);
+    if (NKB == 2 && J < I) lstore_tile<B, D, F32>(knext_of(J), stg, tid);
+    if (J < I) __syncthreads();
   }
   const float tv = 0.5f * pair_sum(tvl);
   if (rvalid && hl == 0) tv_out[(int64_t)t * T + tok0 + i_pos] = tv;
@@ -305,7 +321,8 @@ static mf_status launch_tv(hipStream_t s, const mf_bsr_map *map, const float *W,
                            const RowTable &rt) {
   const int nbw = (g.maxnb + 31) / 32 > 0 ? (g.maxnb + 31) / 32 : 1;
   const size_t smem = tv_smem(B, map->num_heads, nbw);
-  const size_t kb = 2 * (size_t)QKCfg<B, D, F32>::KBYTES;
+  // the static K tile buffers
+  const size_t kb = (tv_two_waves<B, D, F32>() ? 1 : 2) * (size_t)QKCfg<B, D, F32>::KBYTES;
   if (smem + kb > 160 * 1024) return MF_ERR_UNSUPPORTED;
   if (smem + kb > 64 * 1024 &&
       hipFuncSetAttribute(reinterpret_cast<const void *>(&k_tv<B, D, F32, FMT>),
