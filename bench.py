@@ -173,6 +173,54 @@ def tv_bench(torch, mf, wlmod, wl, m, W, cu, cu_dev, args):
     print(json.dumps(line), flush=True)
 
 
+def dense_bench(torch, mf, wlmod, wl, v, cu, cu_dev, args):
+    """Times mf_dense_ref_attention for a receiver layer recomputed in full: the
+    receiver's Ht query heads against the workload's Hkv key/value heads, every
+    causal row (MFMA work 4 d sum_s L_s (L_s + 1) / 2 per query head)."""
+    s = wl.spec
+    dev = v.device
+    Ht = int(wl.W.shape[0])
+    rq, rk, rqb, rkb = wlmod.receiver_qk(wl, Hkr=s.Hkv)
+    if rqb is not None:
+        qr = torch.from_numpy(rqb.view(np.int16)).to(dev).view(torch.bfloat16)
+        kr = torch.from_numpy(rkb.view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        qr, kr = torch.from_numpy(rq).to(dev), torch.from_numpy(rk).to(dev)
+    del rq, rk, rqb, rkb
+    out = torch.empty((Ht, wl.T, s.d), dtype=torch.float32, device=dev)
+    ws = torch.empty(mf.mf_dense_workspace_bytes(s.Hkv, cu, s.d), dtype=torch.uint8, device=dev)
+    for _ in range(max(args.warmup, 1)):
+        mf.mf_dense_ref_attention(qr, kr, v, cu, wl.bias(), out=out, workspace=ws, cu_dev=cu_dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        mf.mf_dense_ref_attention(qr, kr, v, cu, wl.bias(), out=out, workspace=ws, cu_dev=cu_dev)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms_ev = e0.elapsed_time(e1) / args.steps
+    causal = sum(L * (L + 1) // 2 for L in wl.lens)
+    flops = 4.0 * s.d * causal * Ht
+    log(f"dense: {ms_ev:.3f} ms per call ({Ht} query heads, {s.Hkv} kv heads)")
+    line = {
+        "metric": "dense causal attention tokens/s (recomputed receiver layer, all heads)",
+        "value": round(wl.T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if s.qk_dtype == "bf16" else "fp32", "data": "synthetic",
+        "config": {"workload": s.name, "tokens": wl.T, "query_heads": Ht, "kv_heads": int(s.Hkv),
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"kernel": "mf_dense_ref_attention", "bound": "mfma",
+                     "achieved": round(flops / (ms_ev * 1e-3) / 1e12, 1), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(flops / (ms_ev * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "ms_per_launch": round(ms_ev, 4)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -188,6 +236,9 @@ def main():
     ap.add_argument("--tv", action="store_true",
                     help="time mf_tv_distance (translated map vs a synthetic receiver's own map) "
                          "on the compressed map instead of the compress + apply step")
+    ap.add_argument("--dense", action="store_true",
+                    help="time mf_dense_ref_attention (a receiver layer recomputed in full) "
+                         "instead of the compress + apply step")
     ap.add_argument("--paged", type=int, default=0, metavar="P",
                     help="V in a paged pool of P-token pages (mf_apply_translated_paged)")
     ap.add_argument("--chunks", type=int, default=1,
@@ -268,6 +319,10 @@ def main():
     def step():
         compress()
         apply()
+
+    if args.dense:
+        dense_bench(torch, mf, wlmod, wl, v, cu, cu_dev, args)
+        return
 
     for _ in range(args.warmup):
         step()

@@ -6,12 +6,15 @@
 //
 //   O_h = softmax(Q_h K_g^T / sqrt(d) + bias) V_g,  g = h / (Hq / Hkv), causal.
 //
-// One work-group per (query head, 64-row query block), one wave per 32 rows.
-// Key blocks stream through LDS; S^T tiles on MFMA leave each lane holding one
-// query row, so the running max and sum (online softmax) stay in the lane; the
-// probabilities, rounded to bf16, are already in the A-operand layout of the
-// P V product, which runs on MFMA against the transposed V tile.  No map is
-// stored.
+// One work-group per (query head, 128-row query block), one wave per 32 rows.
+// 64-key blocks of K, and of V transposed and block-padded per sequence, stream
+// through two LDS buffer sets (one barrier per block).  S^T tiles on MFMA leave
+// each lane holding one query row, so the running max and sum (online softmax)
+// stay in the lane.  A row's running max moves only when a block's maximum
+// exceeds it by more than 8 (log2 units): the accumulated rows are rescaled
+// rarely, and P stays below 2^8.  P, rounded to bf16, is already in the
+// A-operand layout of the P V product, which runs on MFMA against the
+// transposed V tile.  No map is stored.
 #include <type_traits>
 
 #include "mf_host.hpp"
@@ -19,32 +22,51 @@
 
 namespace mf {
 
-constexpr int kDenseB = 64;
+constexpr int kDenseQB = 128;  // query rows per work-group; row table and V staging block
+constexpr int kDenseKB = 64;   // keys per block
 
 template <int D, bool F32>
 struct DenseCfg {
-  static constexpr int B = kDenseB;
-  using C = QKCfg<B, D, F32>;
-  static constexpr int VPITCH = B * 2 + kLdsPad;
+  static constexpr int QB = kDenseQB, KB = kDenseKB;
+  static constexpr int NT = QB * 2;                 // four waves
+  using C = QKCfg<KB, D, F32>;                      // K tile geometry in LDS
+  static constexpr int KCH = KB * C::CPR / NT;      // 16-byte K chunks per thread
+  static constexpr int VPITCH = KB * 2 + kLdsPad;   // LDS row (one value column) of V^T
   static constexpr int VBYTES = D * VPITCH;
-  static constexpr int VCPR = B * 2 / 16;
-  static constexpr int VNCH = D * VCPR / C::NT;
-  static constexpr int SMEM = C::KBYTES + VBYTES;
-  static_assert(VNCH * C::NT == D * VCPR, "V tile chunks must divide evenly");
+  static constexpr int VCPR = KB * 2 / 16;
+  static constexpr int VCH = D * VCPR / NT;         // 16-byte V chunks per thread
+  static constexpr int SET = C::KBYTES + VBYTES;    // one K + V buffer set
+  static constexpr int SMEM = 2 * SET;
+  static_assert(KCH * NT == KB * C::CPR && VCH * NT == D * VCPR, "tiles must split evenly");
 };
 
+// Whether the 32 query rows [r0, r0 + 32) against the keys [k0, k0 + kb) see
+// every key (no causal mask) with one common offset `off` (log2 units): no sink
+// column, and the local window covers all of the pairs or none of them.
+__device__ __forceinline__ bool dense_uniform(int r0, int k0, int kb, const BiasArgs &b, float &off) {
+  off = 0.f;
+  if (k0 + kb - 1 > r0) return false;
+  if (b.sink2 != 0.f && k0 < b.sink_n) return false;
+  if (b.local2 != 0.f) {
+    const int dmin = r0 - (k0 + kb - 1), dmax = r0 + 31 - k0;
+    if (dmax < b.local_w)
+      off = b.local2;
+    else if (dmin < b.local_w)
+      return false;
+  }
+  return true;
+}
+
 template <int D, bool F32>
-__global__ __launch_bounds__(kDenseB * 2) void k_dense(
+__global__ __launch_bounds__(kDenseQB * 2) __attribute__((amdgpu_waves_per_eu(F32 ? 1 : 2))) void k_dense(
     const void *__restrict__ qv, const void *__restrict__ kv, const uint16_t *__restrict__ vt,
     int64_t T, int32_t Hq, int32_t grp, int32_t NBR, const RowInfo *__restrict__ rows,
     const int32_t *__restrict__ sched, float scale2, BiasArgs bias, float *__restrict__ o) {
-  constexpr int B = kDenseB;
   using DC = DenseCfg<D, F32>;
   using C = typename DC::C;
+  constexpr int QB = DC::QB, KB = DC::KB, NT = DC::NT;
   using E = std::conditional_t<F32, float, uint16_t>;
   __shared__ __attribute__((aligned(16))) char smem[DC::SMEM];
-  char *klds = smem;
-  char *vlds = smem + C::KBYTES;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int m = lane & 31, hl = lane >> 5;
@@ -53,42 +75,58 @@ __global__ __launch_bounds__(kDenseB * 2) void k_dense(
   const int gr = sched[pos];
   const RowInfo ri = rows[gr];
   const int I = ri.blk, L = ri.len;
-  const int i_loc = wave * 32 + m;
-  const int i_pos = I * B + i_loc;
+  const int r0 = I * QB + wave * 32;  // the wave's first query row in the sequence
+  const int i_pos = r0 + m;
   const bool rvalid = i_pos < L;
   const int64_t tok0 = (int64_t)ri.start;
-  const int64_t tpad = (int64_t)NBR * B;
+  const int64_t tpad = (int64_t)NBR * QB;
+  // key blocks up to the work-group's last row, and up to this wave's (0 when
+  // the wave has no row inside the sequence)
+  const int nkb = (min(I * QB + QB, L) - 1) / KB + 1;
+  const int wkb = r0 < L ? min(r0 + 31, L - 1) / KB + 1 : 0;
 
   const E *qh = reinterpret_cast<const E *>(qv) + (int64_t)h * T * D;
-  const char *kh = reinterpret_cast<const char *>(kv) + (int64_t)g * T * D * C::ESZ;
-  const uint16_t *vtg = vt + (int64_t)g * D * tpad;
+  const char *kh = reinterpret_cast<const char *>(kv) + ((int64_t)g * T + tok0) * C::ROWB;
+  const uint16_t *vtg = vt + (int64_t)g * D * tpad + (int64_t)(gr - I) * QB;
   QOp<D, F32> qo;
   load_q<D>(qo, rvalid ? qh + (tok0 + i_pos) * D : nullptr, hl);
 
-  auto gload_v = [&](u32x4 (&stg)[DC::VNCH], int J) {
-    const int64_t col0 = (int64_t)(gr - I + J) * B;
+  // key block J: K rows (zeros past the sequence end) and V^T columns into
+  // registers, then into a buffer set
+  u32x4 kst[DC::KCH], vst[DC::VCH];
+  auto gload = [&](int J) {
+    const int nval = min(KB, L - J * KB);
 #pragma unroll
-    for (int c = 0; c < DC::VNCH; ++c) {
-      const int idx = tid + c * C::NT;
+    for (int c = 0; c < DC::KCH; ++c) {
+      const int idx = tid + c * NT;
+      const int r = idx / C::CPR, col = idx % C::CPR;
+      kst[c] = r < nval ? *reinterpret_cast<const u32x4 *>(kh + (int64_t)(J * KB + r) * C::ROWB + col * 16)
+                        : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int c = 0; c < DC::VCH; ++c) {
+      const int idx = tid + c * NT;
       const int d = idx / DC::VCPR, cc = idx % DC::VCPR;
-      stg[c] = *reinterpret_cast<const u32x4 *>(vtg + (int64_t)d * tpad + col0 + cc * 8);
+      vst[c] = *reinterpret_cast<const u32x4 *>(vtg + (int64_t)d * tpad + J * KB + cc * 8);
     }
   };
-  auto lstore_v = [&](const u32x4 (&stg)[DC::VNCH]) {
+  auto lstore = [&](char *set) {
 #pragma unroll
-    for (int c = 0; c < DC::VNCH; ++c) {
-      const int idx = tid + c * C::NT;
+    for (int c = 0; c < DC::KCH; ++c) {
+      const int idx = tid + c * NT;
+      const int r = idx / C::CPR, col = idx % C::CPR;
+      *reinterpret_cast<u32x4 *>(set + r * C::PITCH + col * 16) = kst[c];
+    }
+#pragma unroll
+    for (int c = 0; c < DC::VCH; ++c) {
+      const int idx = tid + c * NT;
       const int d = idx / DC::VCPR, cc = idx % DC::VCPR;
-      *reinterpret_cast<u32x4 *>(vlds + d * DC::VPITCH + cc * 16) = stg[c];
+      *reinterpret_cast<u32x4 *>(set + C::KBYTES + d * DC::VPITCH + cc * 16) = vst[c];
     }
   };
 
-  u32x4 kst[C::NCH];
-  u32x4 vst[DC::VNCH];
-  gload_tile<B, D, F32>(kst, kh, tok0, min(B, L), tid);
-  gload_v(vst, 0);
-  lstore_tile<B, D, F32>(klds, kst, tid);
-  lstore_v(vst);
+  gload(0);
+  lstore(smem);
   __syncthreads();
 
   f32x16 oacc[D / 32];
@@ -96,64 +134,84 @@ __global__ __launch_bounds__(kDenseB * 2) void k_dense(
   for (int nb = 0; nb < D / 32; ++nb) oacc[nb] = zero16();
   float m_run = -INFINITY, l_run = 0.f;
 
-  for (int J = 0; J <= I; ++J) {
-    if (J < I) {
-      gload_tile<B, D, F32>(kst, kh, tok0 + (int64_t)(J + 1) * B, min(B, L - (J + 1) * B), tid);
-      gload_v(vst, J + 1);
-    }
-    f32x16 acc[B / 32];
-    st_tile<B, D>(acc, klds, qo, lane);
-    const bool plain = plain_tile(I, J, B, bias.sink_n, bias.sink2, bias.local_w, bias.local2);
-    float mx = logits_inplace<B>(acc, plain, rvalid, i_pos, J * B, scale2, bias.sink_n,
-                                 bias.sink2, bias.local_w, bias.local2, lane);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    const float m_new = fmaxf(m_run, mx);
-    const float msafe = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - msafe);
-    float rs = 0.f;
-#pragma unroll
-    for (int mb = 0; mb < B / 32; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pv = rvalid ? fast_exp2(acc[mb][r] - msafe) : 0.f;
-        acc[mb][r] = pv;
-        rs += pv;
+  for (int J = 0; J < nkb; ++J) {
+    const char *cur = smem + (J & 1) * DC::SET;
+    char *nxt = smem + ((J + 1) & 1) * DC::SET;
+    if (J + 1 < nkb) gload(J + 1);
+    if (J < wkb) {
+      f32x16 acc[KB / 32];
+      st_tile<KB, D>(acc, cur, qo, lane);
+      const int k0 = J * KB;
+      float off;
+      const bool uni = dense_uniform(r0, k0, KB, bias, off);
+      float mx;
+      if (uni) {
+        // the scale is positive: the largest logit is the image of the largest score
+        mx = fmaf(pair_max(lane_rawmax<KB>(acc)), scale2, off);
+      } else {
+        mx = pair_max(logits_inplace<KB>(acc, false, rvalid, i_pos, k0, scale2, bias.sink_n,
+                                         bias.sink2, bias.local_w, bias.local2, lane));
       }
-    rs += __shfl_xor(rs, 32, kWave);
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
-    // rescale accumulated rows: row acc_row(r) of this wave belongs to that lane
+      const float m_new = (mx > m_run + 8.f) ? mx : m_run;
+      const float msafe = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - msafe);
+      float rs = 0.f;
+      if (uni) {
+        const float c0 = off - msafe;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float f = __shfl(alpha, acc_row(r, lane), kWave);
+        for (int mb = 0; mb < KB / 32; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < D / 32; ++nb) oacc[nb][r] *= f;
-    }
-    // P (bf16, A operand) x V tile (LDS, B operand)
+          for (int r = 0; r < 16; ++r) {
+            const float pv = fast_exp2(fmaf(acc[mb][r], scale2, c0));
+            acc[mb][r] = pv;
+            rs += pv;
+          }
+      } else {
 #pragma unroll
-    for (int mb = 0; mb < B / 32; ++mb)
+        for (int mb = 0; mb < KB / 32; ++mb)
 #pragma unroll
-      for (int e2 = 0; e2 < 2; ++e2) {
-        u32x4 a;
-        a[0] = pack_bf16x2(acc[mb][8 * e2 + 0], acc[mb][8 * e2 + 1]);
-        a[1] = pack_bf16x2(acc[mb][8 * e2 + 2], acc[mb][8 * e2 + 3]);
-        a[2] = pack_bf16x2(acc[mb][8 * e2 + 4], acc[mb][8 * e2 + 5]);
-        a[3] = pack_bf16x2(acc[mb][8 * e2 + 6], acc[mb][8 * e2 + 7]);
-        const int j0 = mb * 32 + 16 * e2 + 4 * hl;
+          for (int r = 0; r < 16; ++r) {
+            const float pv = rvalid ? fast_exp2(acc[mb][r] - msafe) : 0.f;
+            acc[mb][r] = pv;
+            rs += pv;
+          }
+      }
+      l_run = fmaf(l_run, alpha, pair_sum(rs));
+      m_run = m_new;
+      // rescale the accumulated rows whose max moved (row acc_row(r) of this
+      // wave belongs to that lane)
+      if (wave_ballot(alpha != 1.f)) {
 #pragma unroll
-        for (int nb = 0; nb < D / 32; ++nb) {
-          const char *vp = vlds + (nb * 32 + m) * DC::VPITCH;
-          const uint2 lo = *reinterpret_cast<const uint2 *>(vp + j0 * 2);
-          const uint2 hi = *reinterpret_cast<const uint2 *>(vp + (j0 + 8) * 2);
-          const u32x4 b = u32x4{lo.x, lo.y, hi.x, hi.y};
-          oacc[nb] = mfma_bf16(as_bf16x8(a), as_bf16x8(b), oacc[nb]);
+        for (int r = 0; r < 16; ++r) {
+          const float f = __shfl(alpha, acc_row(r, lane), kWave);
+#pragma unroll
+          for (int nb = 0; nb < D / 32; ++nb) oacc[nb][r] *= f;
         }
       }
-    __syncthreads();
-    if (J < I) {
-      lstore_tile<B, D, F32>(klds, kst, tid);
-      lstore_v(vst);
+      // P (bf16, A operand) x V tile (LDS, B operand)
+      const char *vlds = cur + C::KBYTES;
+#pragma unroll
+      for (int mb = 0; mb < KB / 32; ++mb)
+#pragma unroll
+        for (int e2 = 0; e2 < 2; ++e2) {
+          u32x4 a;
+          a[0] = pack_bf16x2(acc[mb][8 * e2 + 0], acc[mb][8 * e2 + 1]);
+          a[1] = pack_bf16x2(acc[mb][8 * e2 + 2], acc[mb][8 * e2 + 3]);
+          a[2] = pack_bf16x2(acc[mb][8 * e2 + 4], acc[mb][8 * e2 + 5]);
+          a[3] = pack_bf16x2(acc[mb][8 * e2 + 6], acc[mb][8 * e2 + 7]);
+          const int j0 = mb * 32 + 16 * e2 + 4 * hl;
+#pragma unroll
+          for (int nb = 0; nb < D / 32; ++nb) {
+            const char *vp = vlds + (nb * 32 + m) * DC::VPITCH;
+            const uint2 lo = *reinterpret_cast<const uint2 *>(vp + j0 * 2);
+            const uint2 hi = *reinterpret_cast<const uint2 *>(vp + (j0 + 8) * 2);
+            const u32x4 b = u32x4{lo.x, lo.y, hi.x, hi.y};
+            oacc[nb] = mfma_bf16(as_bf16x8(a), as_bf16x8(b), oacc[nb]);
+          }
+        }
     }
+    // the other set held block J - 1, whose readers all passed the last barrier
+    if (J + 1 < nkb) lstore(nxt);
     __syncthreads();
   }
 
@@ -163,7 +221,7 @@ __global__ __launch_bounds__(kDenseB * 2) void k_dense(
   for (int r = 0; r < 16; ++r) {
     const int row = acc_row(r, lane);
     const float f = __shfl(inv, row, kWave);
-    const int ip = I * B + wave * 32 + row;
+    const int ip = r0 + row;
     if (ip < L) {
       float *dst = oh + (tok0 + ip) * D + m;
 #pragma unroll
@@ -172,12 +230,13 @@ __global__ __launch_bounds__(kDenseB * 2) void k_dense(
   }
 }
 
-// V [Hkv][T][D] -> Vt (same kernel shape as the apply path, block 64)
+// V [Hkv][T][D] -> Vt[g][d][NBR * QB]: per sequence block-padded to QB columns,
+// zeros past the sequence end.
 template <int D>
-__global__ __launch_bounds__(256) void k_vtranspose64(const uint16_t *__restrict__ v, int64_t T,
-                                                      const RowInfo *__restrict__ rows,
-                                                      int32_t NBR, uint16_t *__restrict__ vt) {
-  constexpr int B = kDenseB, P = B + 8;
+__global__ __launch_bounds__(256) void k_vtranspose_dense(const uint16_t *__restrict__ v, int64_t T,
+                                                          const RowInfo *__restrict__ rows,
+                                                          int32_t NBR, uint16_t *__restrict__ vt) {
+  constexpr int B = kDenseQB, P = B + 8;
   __shared__ __attribute__((aligned(16))) uint16_t t[D * P];
   const int gr = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
   const RowInfo ri = rows[gr];
@@ -208,12 +267,13 @@ template <int D, bool F32>
 static mf_status launch_dense(hipStream_t s, const void *q, const void *k, const void *v,
                               int32_t Hq, int32_t Hkv, const SeqGeom &g, const BiasArgs &ba,
                               float *o, void *ws, const VtWs &w) {
-  hipLaunchKernelGGL((k_vtranspose64<D>), dim3(g.NBR, Hkv), dim3(256), 0, s,
+  hipLaunchKernelGGL((k_vtranspose_dense<D>), dim3(g.NBR, Hkv), dim3(256), 0, s,
                      reinterpret_cast<const uint16_t *>(v), g.T, at<RowInfo>(ws, w.rt.rows), g.NBR,
                      at<uint16_t>(ws, w.vt));
   if (hip_status() != MF_OK) return MF_ERR_HIP;
   const float scale2 = kLog2e / sqrtf((float)D);
-  hipLaunchKernelGGL((k_dense<D, F32>), dim3((unsigned)((int64_t)g.NBR * Hq)), dim3(kDenseB * 2),
+  if (DenseCfg<D, F32>::SMEM > 160 * 1024) return MF_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL((k_dense<D, F32>), dim3((unsigned)((int64_t)g.NBR * Hq)), dim3(kDenseQB * 2),
                      0, s, q, k, at<uint16_t>(ws, w.vt), g.T, Hq, Hq / Hkv, g.NBR,
                      at<RowInfo>(ws, w.rt.rows), at<int32_t>(ws, w.rt.sched), scale2, ba, o);
   return hip_status();
@@ -226,8 +286,8 @@ using namespace mf;
 extern "C" size_t mf_dense_workspace_bytes(int32_t Hkv, const int32_t *cu, int32_t nseq,
                                            int32_t d) {
   SeqGeom g;
-  if (Hkv <= 0 || !valid_dim(d) || seq_geom(cu, nseq, kDenseB, &g) != MF_OK) return 0;
-  return vt_ws(g, Hkv, kDenseB, d).total;
+  if (Hkv <= 0 || !valid_dim(d) || seq_geom(cu, nseq, kDenseQB, &g) != MF_OK) return 0;
+  return vt_ws(g, Hkv, kDenseQB, d).total;
 }
 
 extern "C" mf_status mf_dense_ref_attention(void *stream, const void *q, const void *k,
@@ -241,16 +301,16 @@ extern "C" mf_status mf_dense_ref_attention(void *stream, const void *q, const v
   if (qk_dtype != MF_BF16 && qk_dtype != MF_FP32) return MF_ERR_UNSUPPORTED;
   if (!valid_dim(d)) return MF_ERR_UNSUPPORTED;
   SeqGeom g;
-  mf_status st = seq_geom(cu_host, nseq, kDenseB, &g);
+  mf_status st = seq_geom(cu_host, nseq, kDenseQB, &g);
   if (st != MF_OK) return st;
   if ((int64_t)g.NBR * Hq > INT32_MAX / 2) return MF_ERR_UNSUPPORTED;
   if (g.T > 0 && (!q || !k || !v || !o)) return MF_ERR_INVALID_ARG;
-  const VtWs w = vt_ws(g, Hkv, kDenseB, d);
+  const VtWs w = vt_ws(g, Hkv, kDenseQB, d);
   if (!ws || ws_bytes < w.total) return MF_ERR_WORKSPACE;
   if (g.NBR == 0) return MF_OK;
   void *wsa = reinterpret_cast<void *>((reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if ((st = launch_rowtable(s, cu_dev, g, kDenseB, wsa, w.rt)) != MF_OK) return st;
+  if ((st = launch_rowtable(s, cu_dev, g, kDenseQB, wsa, w.rt)) != MF_OK) return st;
   const BiasArgs ba = bias_args(bias);
   const bool f32 = qk_dtype == MF_FP32;
   if (d == 64)

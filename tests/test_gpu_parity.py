@@ -231,7 +231,8 @@ def test_full_size_sampled(gpu, idx):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("lens,Hq,Hkv,d,dt", [([256], 2, 2, 64, "fp32"), ([500, 0, 37], 8, 2, 128, "bf16"),
-                                             ([1000], 4, 4, 64, "bf16")])
+                                             ([1000], 4, 4, 64, "bf16"), ([4500, 129], 4, 2, 128, "bf16"),
+                                             ([700, 300], 2, 1, 128, "fp32")])
 def test_dense_attention(gpu, lens, Hq, Hkv, d, dt):
     spec = wlmod.Spec("dense", tuple(lens), Hq, Hq, Hkv, d, 64, 1.0, dt, 100, "gauss", w_var=1.0, seed=55)
     wl = wlmod.make_workload(spec)
