@@ -199,13 +199,13 @@ __global__ __launch_bounds__(kDenseQB * 2) __attribute__((amdgpu_waves_per_eu(F3
           a[1] = pack_bf16x2(acc[mb][8 * e2 + 2], acc[mb][8 * e2 + 3]);
           a[2] = pack_bf16x2(acc[mb][8 * e2 + 4], acc[mb][8 * e2 + 5]);
           a[3] = pack_bf16x2(acc[mb][8 * e2 + 6], acc[mb][8 * e2 + 7]);
-          const int j0 = mb * 32 + 16 * e2 + 4 * hl;
+          // the lane's keys 16 e2 + 4 hl + {0..3, 8..11} of chunk mb: 8
+          // consecutive columns of the quad-swapped V^T rows
+          const int c0 = mb * 32 + 16 * e2 + 8 * hl;
 #pragma unroll
           for (int nb = 0; nb < D / 32; ++nb) {
-            const char *vp = vlds + (nb * 32 + m) * DC::VPITCH;
-            const uint2 lo = *reinterpret_cast<const uint2 *>(vp + j0 * 2);
-            const uint2 hi = *reinterpret_cast<const uint2 *>(vp + (j0 + 8) * 2);
-            const u32x4 b = u32x4{lo.x, lo.y, hi.x, hi.y};
+            const u32x4 b =
+                *reinterpret_cast<const u32x4 *>(vlds + (nb * 32 + m) * DC::VPITCH + c0 * 2);
             oacc[nb] = mfma_bf16(as_bf16x8(a), as_bf16x8(b), oacc[nb]);
           }
         }
@@ -231,7 +231,11 @@ __global__ __launch_bounds__(kDenseQB * 2) __attribute__((amdgpu_waves_per_eu(F3
 }
 
 // V [Hkv][T][D] -> Vt[g][d][NBR * QB]: per sequence block-padded to QB columns,
-// zeros past the sequence end.
+// zeros past the sequence end.  Within every 16 keys the middle two groups of
+// four trade places (keys 4-7 in columns 8-11 and back), so the 8 keys one lane
+// feeds a P V MFMA (4 hl + {0..3, 8..11}) are 8 consecutive columns.
+__device__ __forceinline__ int quad_swap16(int j) { return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1); }
+
 template <int D>
 __global__ __launch_bounds__(256) void k_vtranspose_dense(const uint16_t *__restrict__ v, int64_t T,
                                                           const RowInfo *__restrict__ rows,
@@ -249,8 +253,8 @@ __global__ __launch_bounds__(256) void k_vtranspose_dense(const uint16_t *__rest
     if (j < nval) x = *reinterpret_cast<const u32x4 *>(src + (int64_t)j * D + c * 8);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      t[(c * 8 + 2 * e) * P + j] = (uint16_t)(x[e] & 0xffffu);
-      t[(c * 8 + 2 * e + 1) * P + j] = (uint16_t)(x[e] >> 16);
+      t[(c * 8 + 2 * e) * P + quad_swap16(j)] = (uint16_t)(x[e] & 0xffffu);
+      t[(c * 8 + 2 * e + 1) * P + quad_swap16(j)] = (uint16_t)(x[e] >> 16);
     }
   }
   __syncthreads();
