@@ -399,10 +399,10 @@ struct Apply4Cfg {
   static constexpr int64_t TBYTES = tile_bytes(B, FMT);
   static constexpr int VBYTES = D * B * 2;
   static constexpr int VINST = VBYTES / 1024 / NW;   // 1 KB direct loads per wave per V tile
-  // Ring slots (chunks).  Two, i.e. one chunk ahead: about eight work-groups
-  // read every source tile at nearly the same time, and the L2 does not merge
-  // their concurrent misses.  Deeper prefetch makes all of them miss together
-  // (measured at L = 32K: L2 hit rate 54% with two slots, 12% with four, and
+  // Ring slots (chunks).  Two, i.e. one chunk ahead.  About eight work-groups
+  // of one query block read every source tile, and they hit in the XCD's L2
+  // only while its recent tiles still fit there; deeper prefetch lowers that
+  // hit rate (measured at L = 32K: 54% with two slots, 12% with four, and
   // twice the fabric traffic); 32-row waves with more slots lose the same way.
   static constexpr int NR = 2;
   // loads per unit: row groups x 4 sources, plus 4 scale loads with a block's first unit
