@@ -35,11 +35,23 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_hash() -> str:
+# sources each recorded launch sequence is built from (relative to the repository root)
+KERNEL_SOURCES = {
+    "mf_apply_translated": ("cross_model_sparse_amd/csrc/mf_apply.hip", "cross_model_sparse_amd/csrc/mf_rows.hip",
+                            "cross_model_sparse_amd/csrc/mf_common.hpp", "cross_model_sparse_amd/csrc/mf_host.hpp",
+                            "include/mapflow.h"),
+    "mf_compress_topp": ("cross_model_sparse_amd/csrc/mf_compress.hip", "cross_model_sparse_amd/csrc/mf_qk.hpp",
+                         "cross_model_sparse_amd/csrc/mf_rows.hip", "cross_model_sparse_amd/csrc/mf_common.hpp",
+                         "cross_model_sparse_amd/csrc/mf_host.hpp", "include/mapflow.h"),
+}
+
+
+def source_hash(kernel: str) -> str:
+    """Hash of the sources a recorded kernel sequence is built from: a traffic record
+    taken with other sources does not describe the kernel that runs now."""
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "cross_model_sparse_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
 
@@ -55,7 +67,7 @@ def traffic_record(kernel: str, workload: str):
     except (OSError, ValueError):
         return None
     r = rec.get(kernel, {}).get(workload)
-    if not r or r.get("source_hash") != source_hash():
+    if not r or r.get("source_hash") != source_hash(kernel):
         return None
     return r.get("bytes_per_launch")
 
