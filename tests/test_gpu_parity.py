@@ -180,6 +180,27 @@ def test_max_blocks_per_sequence(gpu):
     check_rows(hm, res, wl.cu_seqlens, wl.T)
 
 
+def test_dense_full_length_sampled(gpu):
+    """Dense attention over a 32768-token sequence (the long-context length: 256
+    query blocks of 128 rows, 512 key blocks of 64) and a ragged second one,
+    GQA 4 on 2, the long-context local window: windows of rows at the start,
+    the middle and the end against the oracle's rows."""
+    spec = wlmod.Spec("dense long", (32768, 1000), 4, 4, 2, 128, 64, 1.0, "bf16", 512, "gauss",
+                      w_var=1.0, seed=91)
+    wl = wlmod.make_workload(spec)
+    q, _ = to_dev_qk(wl, gpu)
+    k = torch.from_numpy(wl.k_bits[:2].copy().view(np.int16)).to(gpu).view(torch.bfloat16)
+    say("dense full length: L = 32768 + 1000, Hq 4, Hkv 2")
+    O = mf.mf_dense_ref_attention(q, k, to_dev_v(wl, gpu), wl.cu_seqlens, wl.bias()).cpu().numpy()
+    kk = wl.k[:2].copy()
+    for s, r0, r1 in [(0, 0, 64), (0, 4000, 4130), (0, 32640, 32768), (1, 870, 1000)]:
+        ranges = {t: ((r0, r1) if t == s else (0, 0)) for t in range(2)}
+        D = orc.dense_attention(wl.q, kk, wl.v, wl.cu_seqlens, wl.bias(), row_ranges=ranges)
+        a, _ = orc.seqs(wl.cu_seqlens)[s]
+        for h in range(4):
+            assert rel_frob(O[h, a + r0:a + r1], D[(h, s)]) <= OUT_RFROB, (s, r0, h)
+
+
 # ---------------------------------------------------------------------------
 # full-size workloads, sampled rows
 # ---------------------------------------------------------------------------
