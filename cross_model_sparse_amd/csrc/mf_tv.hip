@@ -39,7 +39,7 @@ inline size_t tv_smem(int B, int Hs, int nbw) {
 // latency hides behind the MFMAs.  Either way the translated values are
 // subtracted from the receiver's probabilities in place.
 template <int B, int D, bool F32>
-constexpr bool tv_two_waves() { return !F32 && B <= 64; }
+constexpr bool tv_two_waves() { return !F32; }
 
 template <int B, int D, bool F32, int FMT>
 __global__ __launch_bounds__(B * 2)
@@ -192,14 +192,17 @@ __attribute__((amdgpu_waves_per_eu(tv_two_waves<B, D, F32>() ? 2 : 1))) void k_t
   // and 8-key run g, keys 8 g + 4 hl .. + 3 of the lane's row (bf16: 8 bytes of
   // the 16-byte fragment piece; fp8: 4 code bytes and the chunk's scale byte).
   using Raw = std::conditional_t<FP8, uint32_t, uint2>;
-  Raw raw[4][B / 32][4];
-  uint32_t raw_scale[4];
-  float cq[4];
+  // sources per group: two in the two-wave form at B = 128 (their values are
+  // 64 registers), else four
+  constexpr int GS = (TW && B == 128) ? 2 : 4;
+  Raw raw[GS][B / 32][4];
+  uint32_t raw_scale[GS];
+  float cq[GS];
   const int voff = FP8 ? ((i_loc >> 4) * (B / (32 * NP)) * 64 + (i_loc & 15)) * 8 * NP + 4 * hl
                        : ((i_loc >> 4) * (B / 32) * 64 + (i_loc & 15)) * 16 + 8 * hl;
   auto load_group = [&](int q0, int J) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < GS; ++u) {
       const int q = q0 + u;
       int64_t ti = -1;
       if (q < ns) {
@@ -239,7 +242,7 @@ __attribute__((amdgpu_waves_per_eu(tv_two_waves<B, D, F32>() ? 2 : 1))) void k_t
   // the group's translated values, subtracted from the receiver's probabilities
   auto sub_group = [&](f32x16 (&d)[B / 32]) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < GS; ++u) {
 #pragma unroll
       for (int mb = 0; mb < B / 32; ++mb) {
         if constexpr (!FP8) {
@@ -296,7 +299,7 @@ __attribute__((amdgpu_waves_per_eu(tv_two_waves<B, D, F32>() ? 2 : 1))) void k_t
     }
     // receiver minus translated values of the lane's 64 elements, sources four
     // at a time
-    for (int q0 = 0; q0 < ns; q0 += 4) {
+    for (int q0 = 0; q0 < ns; q0 += GS) {
       if (TW || q0 > 0) load_group(q0, J);
       sub_group(acc);
     }
