@@ -30,14 +30,15 @@ inline size_t tv_smem(int B, int Hs, int nbw) {
   return (size_t)Hs * (8 + 4) + (size_t)Hs * nbw * 8 + (size_t)Hs * B * 4 + 64;
 }
 
-// Occupancy.  With bf16 Q/K and B <= 64 a work-group fits half a CU: one K
-// tile buffer (two barriers per block) and 256 VGPRs, so two waves share each
-// SIMD and hide each other's load latency; the sources' tile values load after
-// the block's probabilities.  Otherwise (B = 128, or fp32 Q/K) one wave per SIMD
-// holds the whole register file: two K tile buffers (one barrier per block),
-// and the first four sources' tile values load before the QK^T tile, so their
-// latency hides behind the MFMAs.  Either way the translated values are
-// subtracted from the receiver's probabilities in place.
+// Occupancy.  With bf16 Q/K a work-group fits half a CU: one K tile buffer (two
+// barriers per block) and 256 VGPRs, so two waves share each SIMD and hide each
+// other's load latency; the sources' tile values load after the block's
+// probabilities, two sources at a time at B = 128 (four would need 128
+// registers of tile values).  With fp32 Q/K one wave per SIMD holds the whole
+// register file: two K tile buffers (one barrier per block), and the first four
+// sources' tile values load before the QK^T tile, so their latency hides behind
+// the MFMAs.  Either way the translated values are subtracted from the
+// receiver's probabilities in place.
 template <int B, int D, bool F32>
 constexpr bool tv_two_waves() { return !F32; }
 
