@@ -37,11 +37,16 @@ struct SelectCfg {
   static constexpr int OFF_BM = OFF_TSUM + (C::NT + 1) * 8;  // tsum[NT + 1]
   static constexpr int OFF_KC = OFF_BM + 32 * 4;             // bm[32]
   static constexpr int EPI = OFF_KC + 16;
-  static constexpr int SMEM = 2 * C::KBYTES > EPI ? 2 * C::KBYTES : EPI;  // two K tiles
+  // K tile buffers: one for bf16 Q/K with B <= 64, so that a work-group takes a
+  // third of a CU and three waves share each SIMD (two barriers per block);
+  // else two (one barrier per block) and two waves per SIMD
+  static constexpr int NKB = (!F32 && B <= 64) ? 1 : 2;
+  static constexpr int WAVES = F32 ? 1 : (NKB == 1 ? 3 : 2);
+  static constexpr int SMEM = NKB * C::KBYTES > EPI ? NKB * C::KBYTES : EPI;
 };
 
 template <int B, int D, bool F32>
-__global__ __launch_bounds__(B * 2) __attribute__((amdgpu_waves_per_eu(F32 ? 1 : 2))) void k_select(
+__global__ __launch_bounds__(B * 2) __attribute__((amdgpu_waves_per_eu(SelectCfg<B, D, F32>::WAVES))) void k_select(
     const void *__restrict__ qv, const void *__restrict__ kv, int64_t T, int32_t Hs, int32_t NBR,
     const RowInfo *__restrict__ rows, const int32_t *__restrict__ sched,
     const int64_t *__restrict__ pbase, int64_t ptot, float scale2, BiasArgs bias, double p,
@@ -78,8 +83,11 @@ __global__ __launch_bounds__(B * 2) __attribute__((amdgpu_waves_per_eu(F32 ? 1 :
   QOp<D, F32> qo;
   load_q<D>(qo, rvalid ? qh + (tok0 + i_pos) * D : nullptr, hl);
 
-  // K tiles alternate between two LDS buffers: block J is read from buffer
-  // J & 1 while block J + 1 is written to the other one, one barrier per block.
+  // Block J + 1 of K loads into registers while block J is multiplied.  Two
+  // buffers: it is stored into the other buffer, one barrier per block.  One
+  // buffer: stored after a barrier (every wave's reads of block J done), and
+  // the barrier that ends the step makes it visible.
+  constexpr int NKB = SelectCfg<B, D, F32>::NKB;
   u32x4 stg[C::NCH];
   gload_tile<B, D, F32>(stg, kh, tok0, min(B, L), tid);
   lstore_tile<B, D, F32>(smem, stg, tid);
@@ -87,11 +95,15 @@ __global__ __launch_bounds__(B * 2) __attribute__((amdgpu_waves_per_eu(F32 ? 1 :
 
   float m_run = -INFINITY;
   for (int J = 0; J <= I; ++J) {
-    const char *kcur = smem + (J & 1) * C::KBYTES;
-    char *knext = smem + ((J + 1) & 1) * C::KBYTES;
+    const char *kcur = smem + (NKB == 2 ? (J & 1) * C::KBYTES : 0);
+    char *knext = smem + (NKB == 2 ? ((J + 1) & 1) * C::KBYTES : 0);
     if (J < I) gload_tile<B, D, F32>(stg, kh, tok0 + (int64_t)(J + 1) * B, min(B, L - (J + 1) * B), tid);
     f32x16 acc[B / 32];
     st_tile<B, D>(acc, kcur, qo, lane);
+    if (NKB == 1 && J < I) {
+      __syncthreads();
+      lstore_tile<B, D, F32>(knext, stg, tid);
+    }
     float lse, off;
     if (uniform_tile(I, J, B, bias.sink_n, bias.sink2, bias.local_w, bias.local2, off)) {
       // the scale is positive: the largest scaled logit is the image of the
@@ -111,7 +123,7 @@ __global__ __launch_bounds__(B * 2) __attribute__((amdgpu_waves_per_eu(F32 ? 1 :
     if (hl == 0) part[(int64_t)J * B + i_loc] = lse;
     m_run = fmaxf(m_run, lse);
     // the other buffer held block J - 1, whose readers all passed the last barrier
-    if (J < I) lstore_tile<B, D, F32>(knext, stg, tid);
+    if (NKB == 2 && J < I) lstore_tile<B, D, F32>(knext, stg, tid);
     __syncthreads();
   }
 
