@@ -14,6 +14,11 @@
  *                           for every target head, without a dense L x L map in
  *                           device memory.  MapFlow §3.3 (linear head mapping),
  *                           §5.4 (fused retrieval kernel).
+ *   mf_apply_translated_paged
+ *                           the same retrieval with V in a paged pool behind a
+ *                           page table, optionally over one query window per
+ *                           sequence (chunked prefill).  MapFlow §6 (paged
+ *                           memory and varlen batches in the serving stack).
  *   mf_prefix_dedupe        block-rows whose query/key prefix repeats an earlier
  *                           sequence's, so compression computes them once and
  *                           both sides read the first copy.  MapFlow §5.3 (Block
