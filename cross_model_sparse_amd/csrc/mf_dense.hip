@@ -6,7 +6,7 @@
 //
 //   O_h = softmax(Q_h K_g^T / sqrt(d) + bias) V_g,  g = h / (Hq / Hkv), causal.
 //
-// One work-group per (query head, 128-row query block), one wave per 32 rows.
+// One work-group per (query head, 256-row query block), one wave per 32 rows.
 // 64-key blocks of K, and of V transposed and block-padded per sequence, stream
 // through two LDS buffer sets (one barrier per block).  S^T tiles on MFMA leave
 // each lane holding one query row, so the running max and sum (online softmax)
@@ -22,13 +22,13 @@
 
 namespace mf {
 
-constexpr int kDenseQB = 128;  // query rows per work-group; row table and V staging block
+constexpr int kDenseQB = 256;  // query rows per work-group; row table and V staging block
 constexpr int kDenseKB = 64;   // keys per block
 
 template <int D, bool F32>
 struct DenseCfg {
   static constexpr int QB = kDenseQB, KB = kDenseKB;
-  static constexpr int NT = QB * 2;                 // four waves
+  static constexpr int NT = QB * 2;                 // eight waves
   using C = QKCfg<KB, D, F32>;                      // K tile geometry in LDS
   static constexpr int KCH = KB * C::CPR / NT;      // 16-byte K chunks per thread
   static constexpr int VPITCH = KB * 2 + kLdsPad;   // LDS row (one value column) of V^T
@@ -58,7 +58,7 @@ __device__ __forceinline__ bool dense_uniform(int r0, int k0, int kb, const Bias
 }
 
 template <int D, bool F32>
-__global__ __launch_bounds__(kDenseQB * 2) __attribute__((amdgpu_waves_per_eu(F32 ? 1 : 2))) void k_dense(
+__global__ __launch_bounds__(kDenseQB * 2) __attribute__((amdgpu_waves_per_eu(2))) void k_dense(
     const void *__restrict__ qv, const void *__restrict__ kv, const uint16_t *__restrict__ vt,
     int64_t T, int32_t Hq, int32_t grp, int32_t NBR, const RowInfo *__restrict__ rows,
     const int32_t *__restrict__ sched, float scale2, BiasArgs bias, float *__restrict__ o) {
@@ -290,7 +290,7 @@ using namespace mf;
 extern "C" size_t mf_dense_workspace_bytes(int32_t Hkv, const int32_t *cu, int32_t nseq,
                                            int32_t d) {
   SeqGeom g;
-  if (Hkv <= 0 || !valid_dim(d) || seq_geom(cu, nseq, kDenseQB, &g) != MF_OK) return 0;
+  if (Hkv <= 0 || !valid_dim(d) || seq_geom_blocks(cu, nseq, kDenseQB, &g) != MF_OK) return 0;
   return vt_ws(g, Hkv, kDenseQB, d).total;
 }
 
@@ -305,7 +305,7 @@ extern "C" mf_status mf_dense_ref_attention(void *stream, const void *q, const v
   if (qk_dtype != MF_BF16 && qk_dtype != MF_FP32) return MF_ERR_UNSUPPORTED;
   if (!valid_dim(d)) return MF_ERR_UNSUPPORTED;
   SeqGeom g;
-  mf_status st = seq_geom(cu_host, nseq, kDenseQB, &g);
+  mf_status st = seq_geom_blocks(cu_host, nseq, kDenseQB, &g);
   if (st != MF_OK) return st;
   if ((int64_t)g.NBR * Hq > INT32_MAX / 2) return MF_ERR_UNSUPPORTED;
   if (g.T > 0 && (!q || !k || !v || !o)) return MF_ERR_INVALID_ARG;

@@ -28,11 +28,11 @@ constexpr int64_t tile_bytes(int B, int fmt) {
   return fmt == MF_TILE_MXFP8 ? (int64_t)B * B + (int64_t)B * (B / 32) : (int64_t)B * B * 2;
 }
 
-// Validates host offsets and fills the geometry. MF_ERR_UNSUPPORTED for too many
-// key blocks in one sequence.
-inline mf_status seq_geom(const int32_t *cu, int32_t nseq, int32_t B, SeqGeom *g) {
-  if (nseq < 0 || !cu) return MF_ERR_INVALID_ARG;
-  if (!valid_block(B)) return MF_ERR_UNSUPPORTED;
+// Validates host offsets and fills the geometry for blocks of B tokens (any
+// B > 0; the caller checks that B suits its kernels). MF_ERR_UNSUPPORTED for
+// too many blocks in one sequence.
+inline mf_status seq_geom_blocks(const int32_t *cu, int32_t nseq, int32_t B, SeqGeom *g) {
+  if (nseq < 0 || !cu || B <= 0) return MF_ERR_INVALID_ARG;
   if (cu[0] != 0) return MF_ERR_INVALID_ARG;
   SeqGeom r;
   r.nseq = nseq;
@@ -51,6 +51,13 @@ inline mf_status seq_geom(const int32_t *cu, int32_t nseq, int32_t B, SeqGeom *g
   r.T = cu[nseq];
   *g = r;
   return MF_OK;
+}
+
+// The same for a map's block size B (32, 64 or 128).
+inline mf_status seq_geom(const int32_t *cu, int32_t nseq, int32_t B, SeqGeom *g) {
+  if (nseq < 0 || !cu) return MF_ERR_INVALID_ARG;
+  if (!valid_block(B)) return MF_ERR_UNSUPPORTED;
+  return seq_geom_blocks(cu, nseq, B, g);
 }
 
 struct BiasArgs {

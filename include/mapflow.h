@@ -297,7 +297,7 @@ mf_status mf_apply_translated_paged(void *stream, const mf_bsr_map *map, const f
                                     void *workspace, size_t workspace_bytes);
 
 /* Device workspace bytes mf_dense_ref_attention needs (transposed V, padded per
- * sequence to 128-token blocks, as for apply).  0 if invalid. */
+ * sequence to 256-token blocks).  0 if invalid. */
 size_t mf_dense_workspace_bytes(int32_t Hkv, const int32_t *cu_seqlens_host, int32_t nseq,
                                 int32_t d);
 
