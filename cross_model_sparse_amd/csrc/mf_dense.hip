@@ -15,6 +15,13 @@
 // rarely, and P stays below 2^8.  P, rounded to bf16, is already in the
 // A-operand layout of the P V product, which runs on MFMA against the
 // transposed V tile.  No map is stored.
+//
+// With bf16 inputs, Q is scaled by log2(e)/sqrt(d) once (one more bf16
+// rounding per element).  Blocks with one offset for all of their pairs then
+// take a short form: the Q K^T accumulators start from (offset - running max)
+// of the lane's row, so they leave the MFMA as exponents; P = exp2 of them,
+// with no per-block maximum, and the row sum is taken from the bf16 P.  A
+// block whose row sum passes 2^16 is redone in the exact form.
 #include <type_traits>
 
 #include "mf_host.hpp"
@@ -57,6 +64,44 @@ __device__ __forceinline__ bool dense_uniform(int r0, int k0, int kb, const Bias
   return true;
 }
 
+// Multiplies every bf16 element of the lane's Q half-row by `s` (RNE).
+template <int D>
+__device__ __forceinline__ void scale_q(QOp<D, false> &qo, float s) {
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t x = qo.v[c][w];
+      qo.v[c][w] = pack_bf16x2(__uint_as_float(x << 16) * s, __uint_as_float(x & 0xffff0000u) * s);
+    }
+}
+
+// S^T tile for the wave's 32 query rows against the B staged keys, as
+// st_tile, with every accumulator starting from `seed` instead of 0.
+template <int B, int D>
+__device__ __forceinline__ void st_tile_seeded(f32x16 (&acc)[B / 32], const char *klds,
+                                               const QOp<D, false> &qo, int lane,
+                                               const f32x16 &seed) {
+  using C = QKCfg<B, D, false>;
+  const int m = lane & 31, hl = lane >> 5;
+  const char *rowp = klds + m * C::PITCH + hl * D;
+#pragma unroll
+  for (int mb = 0; mb < B / 32; ++mb) acc[mb] = seed;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+    for (int mb = 0; mb < B / 32; ++mb) {
+      u32x4 a = *reinterpret_cast<const u32x4 *>(rowp + mb * 32 * C::PITCH + ks * 16);
+      acc[mb] = mfma_bf16(as_bf16x8(a), as_bf16x8(qo.v[ks]), acc[mb]);
+    }
+}
+
+// acc + lo + hi of a packed bf16 pair (one dot2 against [1, 1]).
+__device__ __forceinline__ float add_bf16x2(uint32_t w, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w),
+                                         __builtin_bit_cast(bf16x2, 0x3f803f80u), acc, false);
+}
+
 template <int D, bool F32>
 __global__ __launch_bounds__(kDenseQB * 2) __attribute__((amdgpu_waves_per_eu(2))) void k_dense(
     const void *__restrict__ qv, const void *__restrict__ kv, const uint16_t *__restrict__ vt,
@@ -90,6 +135,8 @@ __global__ __launch_bounds__(kDenseQB * 2) __attribute__((amdgpu_waves_per_eu(2)
   const uint16_t *vtg = vt + (int64_t)g * D * tpad + (int64_t)(gr - I) * QB;
   QOp<D, F32> qo;
   load_q<D>(qo, rvalid ? qh + (tok0 + i_pos) * D : nullptr, hl);
+  if constexpr (!F32) scale_q<D>(qo, scale2);
+  const float sc = F32 ? scale2 : 1.f;  // scale still due on the MFMA's scores
 
   // key block J: K rows (zeros past the sequence end) and V^T columns into
   // registers, then into a buffer set
@@ -133,6 +180,9 @@ __global__ __launch_bounds__(kDenseQB * 2) __attribute__((amdgpu_waves_per_eu(2)
 #pragma unroll
   for (int nb = 0; nb < D / 32; ++nb) oacc[nb] = zero16();
   float m_run = -INFINITY, l_run = 0.f;
+  // accumulator seed of the short form: offset - m_run of the lane's row
+  float seedv = -INFINITY;
+  f32x16 seed = zero16();
 
   for (int J = 0; J < nkb; ++J) {
     const char *cur = smem + (J & 1) * DC::SET;
@@ -140,53 +190,94 @@ __global__ __launch_bounds__(kDenseQB * 2) __attribute__((amdgpu_waves_per_eu(2)
     if (J + 1 < nkb) gload(J + 1);
     if (J < wkb) {
       f32x16 acc[KB / 32];
-      st_tile<KB, D>(acc, cur, qo, lane);
+      u32x4 pa[KB / 32][2];  // P in bf16: the lane's A operands of P V
       const int k0 = J * KB;
       float off;
       const bool uni = dense_uniform(r0, k0, KB, bias, off);
-      float mx;
-      if (uni) {
-        // the scale is positive: the largest logit is the image of the largest score
-        mx = fmaf(pair_max(lane_rawmax<KB>(acc)), scale2, off);
-      } else {
-        mx = pair_max(logits_inplace<KB>(acc, false, rvalid, i_pos, k0, scale2, bias.sink_n,
-                                         bias.sink2, bias.local_w, bias.local2, lane));
-      }
-      const float m_new = (mx > m_run + 8.f) ? mx : m_run;
-      const float msafe = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - msafe);
-      float rs = 0.f;
-      if (uni) {
-        const float c0 = off - msafe;
+      bool done = false;
+      if constexpr (!F32) {
+        if (uni && !wave_ballot(m_run == -INFINITY)) {
+          const float want = off - m_run;
+          if (wave_ballot(want != seedv)) {
+            // rare (a moved max or a new offset): kept as a branch, not selects
+            asm volatile("" ::: "memory");
+            seedv = want;
 #pragma unroll
-        for (int mb = 0; mb < KB / 32; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float pv = fast_exp2(fmaf(acc[mb][r], scale2, c0));
-            acc[mb][r] = pv;
-            rs += pv;
+            for (int r = 0; r < 16; ++r) seed[r] = seedv;
           }
-      } else {
+          st_tile_seeded<KB, D>(acc, cur, qo, lane, seed);
+          float rs = 0.f;
 #pragma unroll
-        for (int mb = 0; mb < KB / 32; ++mb)
+          for (int mb = 0; mb < KB / 32; ++mb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float pv = rvalid ? fast_exp2(acc[mb][r] - msafe) : 0.f;
-            acc[mb][r] = pv;
-            rs += pv;
+            for (int e2 = 0; e2 < 2; ++e2)
+#pragma unroll
+              for (int k = 0; k < 4; ++k) {
+                pa[mb][e2][k] = pack_bf16x2(fast_exp2(acc[mb][8 * e2 + 2 * k]),
+                                            fast_exp2(acc[mb][8 * e2 + 2 * k + 1]));
+                rs = add_bf16x2(pa[mb][e2][k], rs);
+              }
+          rs = pair_sum(rs);
+          // P below 2^16 in every row (inf and NaN fail the test): the block stands
+          if (!wave_ballot(!(rs <= 65536.f))) {
+            l_run += rs;
+            done = true;
           }
-      }
-      l_run = fmaf(l_run, alpha, pair_sum(rs));
-      m_run = m_new;
-      // rescale the accumulated rows whose max moved (row acc_row(r) of this
-      // wave belongs to that lane)
-      if (wave_ballot(alpha != 1.f)) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float f = __shfl(alpha, acc_row(r, lane), kWave);
-#pragma unroll
-          for (int nb = 0; nb < D / 32; ++nb) oacc[nb][r] *= f;
         }
+      }
+      if (!done) {
+        st_tile<KB, D>(acc, cur, qo, lane);
+        float mx;
+        if (uni) {
+          // the scale is positive: the largest logit is the image of the largest score
+          mx = fmaf(pair_max(lane_rawmax<KB>(acc)), sc, off);
+        } else {
+          mx = pair_max(logits_inplace<KB>(acc, false, rvalid, i_pos, k0, sc, bias.sink_n,
+                                           bias.sink2, bias.local_w, bias.local2, lane));
+        }
+        const float m_new = (mx > m_run + 8.f) ? mx : m_run;
+        const float msafe = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = fast_exp2(m_run - msafe);
+        float rs = 0.f;
+        if (uni) {
+          const float c0 = off - msafe;
+#pragma unroll
+          for (int mb = 0; mb < KB / 32; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const float pv = fast_exp2(fmaf(acc[mb][r], sc, c0));
+              acc[mb][r] = pv;
+              rs += pv;
+            }
+        } else {
+#pragma unroll
+          for (int mb = 0; mb < KB / 32; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const float pv = rvalid ? fast_exp2(acc[mb][r] - msafe) : 0.f;
+              acc[mb][r] = pv;
+              rs += pv;
+            }
+        }
+        l_run = fmaf(l_run, alpha, pair_sum(rs));
+        m_run = m_new;
+        // rescale the accumulated rows whose max moved (row acc_row(r) of this
+        // wave belongs to that lane)
+        if (wave_ballot(alpha != 1.f)) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float f = __shfl(alpha, acc_row(r, lane), kWave);
+#pragma unroll
+            for (int nb = 0; nb < D / 32; ++nb) oacc[nb][r] *= f;
+          }
+        }
+#pragma unroll
+        for (int mb = 0; mb < KB / 32; ++mb)
+#pragma unroll
+          for (int e2 = 0; e2 < 2; ++e2)
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              pa[mb][e2][k] = pack_bf16x2(acc[mb][8 * e2 + 2 * k], acc[mb][8 * e2 + 2 * k + 1]);
       }
       // P (bf16, A operand) x V tile (LDS, B operand)
       const char *vlds = cur + C::KBYTES;
@@ -194,11 +285,6 @@ __global__ __launch_bounds__(kDenseQB * 2) __attribute__((amdgpu_waves_per_eu(2)
       for (int mb = 0; mb < KB / 32; ++mb)
 #pragma unroll
         for (int e2 = 0; e2 < 2; ++e2) {
-          u32x4 a;
-          a[0] = pack_bf16x2(acc[mb][8 * e2 + 0], acc[mb][8 * e2 + 1]);
-          a[1] = pack_bf16x2(acc[mb][8 * e2 + 2], acc[mb][8 * e2 + 3]);
-          a[2] = pack_bf16x2(acc[mb][8 * e2 + 4], acc[mb][8 * e2 + 5]);
-          a[3] = pack_bf16x2(acc[mb][8 * e2 + 6], acc[mb][8 * e2 + 7]);
           // the lane's keys 16 e2 + 4 hl + {0..3, 8..11} of chunk mb: 8
           // consecutive columns of the quad-swapped V^T rows
           const int c0 = mb * 32 + 16 * e2 + 8 * hl;
@@ -206,7 +292,7 @@ __global__ __launch_bounds__(kDenseQB * 2) __attribute__((amdgpu_waves_per_eu(2)
           for (int nb = 0; nb < D / 32; ++nb) {
             const u32x4 b =
                 *reinterpret_cast<const u32x4 *>(vlds + (nb * 32 + m) * DC::VPITCH + c0 * 2);
-            oacc[nb] = mfma_bf16(as_bf16x8(a), as_bf16x8(b), oacc[nb]);
+            oacc[nb] = mfma_bf16(as_bf16x8(pa[mb][e2]), as_bf16x8(b), oacc[nb]);
           }
         }
     }

@@ -273,6 +273,35 @@ def test_dense_attention(gpu, lens, Hq, Hkv, d, dt):
             assert rel_frob(O[h, a:a + L], ref) <= OUT_RFROB
 
 
+@pytest.mark.parametrize("rise", [12.0, 20.0])
+def test_dense_rising_logits(gpu, rise):
+    """Logits that climb by about `rise` (log2 units) from one 64-key block to the
+    next, so a block's maximum passes the running one by 8 to 16 (the running max
+    lags, P grows) or by more than 16 (the block is redone with a rescale)."""
+    rng = np.random.default_rng(58)
+    lens, d, Hq, Hkv = [448, 130], 128, 2, 1
+    cu = np.array([0, lens[0], lens[0] + lens[1]], dtype=np.int32)
+    T = int(cu[-1])
+    u = rng.standard_normal(d)
+    step = rise / (np.sqrt(d) * np.log2(np.e))  # |u|^2 ~ d: q.k/sqrt(d) in log2 units ~ c * 16.3
+    c = np.concatenate([step * (np.arange(L) // 64) for L in lens])
+    q = u[None, None, :] + 0.5 * rng.standard_normal((Hq, T, d))
+    k = c[None, :, None] * u[None, None, :] + 0.5 * rng.standard_normal((Hkv, T, d))
+    v = rng.standard_normal((Hkv, T, d))
+    bits = [wlmod.f32_to_bf16_bits(x.astype(np.float32)) for x in (q, k, v)]
+    qv, kv, vv = (wlmod.bf16_bits_to_f32(b).astype(np.float64) for b in bits)
+    dq, dk, dv = (torch.from_numpy(b.view(np.int16)).to(gpu).view(torch.bfloat16) for b in bits)
+    bias = dict(sink_n=4, sink_bias=4.0, local_w=100, local_bias=2.0)
+    say(f"dense rising logits: {rise} per block, lens={lens}")
+    O = mf.mf_dense_ref_attention(dq, dk, dv, cu, bias).cpu().numpy()
+    D = orc.dense_attention(qv, kv, vv, cu, bias)
+    for (h, s), ref in D.items():
+        a, L = orc.seqs(cu)[s]
+        err = rel_frob(O[h, a:a + L], ref)
+        say(f"  head {h} seq {s}: {err:.2e}")
+        assert err <= OUT_RFROB
+
+
 # ---------------------------------------------------------------------------
 # shared-prefix block-rows (MapFlow §5.3)
 # ---------------------------------------------------------------------------
