@@ -306,6 +306,9 @@ size_t mf_dense_workspace_bytes(int32_t Hkv, const int32_t *cu_seqlens_host, int
  *   O_h = softmax(Q_h K_g^T / sqrt(d) + bias) V_g,   g = h / (Hq / Hkv).
  * q [Hq][T][d] and k [Hkv][T][d] in qk_dtype; v [Hkv][T][d] bf16; o [Hq][T][d]
  * fp32.  No map is read or written.
+ * Precision: products on bf16 MFMA with fp32 accumulation; P is rounded to
+ * bf16 for the P V product.  With bf16 q, q times log2(e)/sqrt(d) is rounded
+ * to bf16 once before the product (fp32 q keeps the scale in fp32).
  * Errors: MF_ERR_INVALID_ARG, MF_ERR_UNSUPPORTED, MF_ERR_WORKSPACE, MF_ERR_HIP. */
 mf_status mf_dense_ref_attention(void *stream, const void *q, const void *k, const void *v,
                                  mf_dtype qk_dtype, int32_t Hq, int32_t Hkv, int32_t d,
