@@ -273,6 +273,29 @@ def test_dense_attention(gpu, lens, Hq, Hkv, d, dt):
             assert rel_frob(O[h, a:a + L], ref) <= OUT_RFROB
 
 
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+def test_dense_attention_no_bias(gpu, dt):
+    """No sink and no local window: every block below the diagonal is uniform,
+    block 0 included, so a row's first block meets an unset running max."""
+    spec = wlmod.Spec("dense no bias", (300, 65, 1), 2, 2, 1, 128, 64, 1.0, dt, 100, "gauss",
+                      w_var=1.0, seed=56, sink_bias=0.0, local_bias=0.0)
+    wl = wlmod.make_workload(spec)
+    q, _ = to_dev_qk(wl, gpu)
+    kk = wl.k[:1].copy()  # K from the first drawn head, one K/V head
+    if dt == "bf16":
+        k = torch.from_numpy(wl.k_bits[:1].copy().view(np.int16)).to(gpu).view(torch.bfloat16)
+    else:
+        k = torch.from_numpy(kk).to(gpu)
+    say(f"dense no bias {dt}")
+    O = mf.mf_dense_ref_attention(q, k, to_dev_v(wl, gpu), wl.cu_seqlens, wl.bias()).cpu().numpy()
+    D = orc.dense_attention(wl.q, kk, wl.v, wl.cu_seqlens, wl.bias())
+    for (h, s), ref in D.items():
+        a, L = orc.seqs(wl.cu_seqlens)[s]
+        err = rel_frob(O[h, a:a + L], ref)
+        say(f"  head {h} seq {s}: {err:.2e}")
+        assert err <= OUT_RFROB
+
+
 @pytest.mark.parametrize("rise", [12.0, 20.0])
 def test_dense_rising_logits(gpu, rise):
     """Logits that climb by about `rise` (log2 units) from one 64-key block to the
