@@ -64,6 +64,16 @@ __device__ __forceinline__ bool dense_uniform(int r0, int k0, int kb, const Bias
   return true;
 }
 
+// Whether the rows [r0, r0 + 32) against the keys [k0, k0 + kb) see every key
+// with no sink column, while the local window covers only part of the pairs:
+// the one bias left is the window's, element by element.
+__device__ __forceinline__ bool dense_window_edge(int r0, int k0, int kb, const BiasArgs &b) {
+  if (k0 + kb - 1 > r0 || b.local2 == 0.f) return false;
+  if (b.sink2 != 0.f && k0 < b.sink_n) return false;
+  const int dmin = r0 - (k0 + kb - 1), dmax = r0 + 31 - k0;
+  return dmin < b.local_w && b.local_w <= dmax;
+}
+
 // Multiplies every bf16 element of the lane's Q half-row by `s` (RNE).
 template <int D>
 __device__ __forceinline__ void scale_q(QOp<D, false> &qo, float s) {
@@ -194,9 +204,12 @@ __global__ __launch_bounds__(kDenseQB * 2) __attribute__((amdgpu_waves_per_eu(2)
       const int k0 = J * KB;
       float off;
       const bool uni = dense_uniform(r0, k0, KB, bias, off);
+      // window-edge blocks take the short form too (off = 0), plus the window
+      // bias element by element
+      const bool edge = !uni && dense_window_edge(r0, k0, KB, bias);
       bool done = false;
       if constexpr (!F32) {
-        if (uni && !wave_ballot(m_run == -INFINITY)) {
+        if ((uni || edge) && !wave_ballot(m_run == -INFINITY)) {
           const float want = off - m_run;
           if (wave_ballot(want != seedv)) {
             // rare (a moved max or a new offset): kept as a branch, not selects
@@ -206,6 +219,16 @@ __global__ __launch_bounds__(kDenseQB * 2) __attribute__((amdgpu_waves_per_eu(2)
             for (int r = 0; r < 16; ++r) seed[r] = seedv;
           }
           st_tile_seeded<KB, D>(acc, cur, qo, lane, seed);
+          if (edge) {
+            // key k0 + mb * 32 + acc_row(r) is inside the window (i - j < w)
+            // when mb * 32 + 8 (r / 4) + r % 4 > i - w - k0 - 4 hl
+            const int t = i_pos - bias.local_w - k0 - 4 * hl;
+#pragma unroll
+            for (int mb = 0; mb < KB / 32; ++mb)
+#pragma unroll
+              for (int r = 0; r < 16; ++r)
+                acc[mb][r] += (mb * 32 + 8 * (r >> 2) + (r & 3) > t) ? bias.local2 : 0.f;
+          }
           float rs = 0.f;
 #pragma unroll
           for (int mb = 0; mb < KB / 32; ++mb)
