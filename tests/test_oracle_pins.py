@@ -165,6 +165,27 @@ def test_dense_gqa_matches_sdpa():
         np.testing.assert_allclose(D[(h, 0)], sdpa_reference(q[h], k[g], v[g], BIAS), rtol=1e-10, atol=1e-12)
 
 
+def test_dense_row_ranges_match_sdpa_rows():
+    """Dense attention restricted to a row window per sequence (the sampled
+    full-length check uses this) equals the same rows of torch's
+    scaled_dot_product_attention over the whole sequence, GQA included; an
+    empty window gives no rows."""
+    Hq, Hkv, d = 4, 2, 8
+    lens = [70, 33, 5]
+    cu = np.array([0, 70, 103, 108], dtype=np.int32)
+    T = int(cu[-1])
+    q, k, v = rand((Hq, T, d), 41), rand((Hkv, T, d), 42), rand((Hkv, T, d), 43)
+    ranges = {0: (17, 51), 1: (0, 33), 2: (3, 3)}
+    D = orc.dense_attention(q, k, v, cu, BIAS, row_ranges=ranges)
+    for h in range(Hq):
+        g = h // 2
+        for s, (a, L) in enumerate(orc.seqs(cu)):
+            r0, r1 = ranges[s]
+            ref = sdpa_reference(q[h, a:a + L], k[g, a:a + L], v[g, a:a + L], BIAS)[r0:r1]
+            assert D[(h, s)].shape == (r1 - r0, d)
+            np.testing.assert_allclose(D[(h, s)], ref, rtol=1e-10, atol=1e-12)
+
+
 def test_identity_w_is_per_head_reuse():
     """W = I: O_h = renorm(A_hat_h) V_h, the cached-map reuse path. The reference here
     builds the dense sparsified map from SDPA-style softmax (torch), zeroes dropped
@@ -426,6 +447,27 @@ def test_prefix_alias_bruteforce(seed):
     got = orc.prefix_alias(q, k, cu, B).tolist()
     assert got == _bf_alias(q, k, cu, B)
     assert got != list(range(len(got)))  # something is shared
+
+
+def test_row_subsets_match_the_full_computation():
+    """compress(rows=...) and apply(rows=...), which the chunked-prefill and
+    sampled checks use, return exactly the full computation's results on the
+    requested (sequence, block-row) pairs, and nothing else."""
+    wl = wlmod.small_variant(5, [200, 96, 33], Hs=2, Ht=3, Hkv=3)
+    B = 32
+    full = orc.compress(wl.q, wl.k, wl.cu_seqlens, B, 0.9, wl.bias())
+    allrows = orc.block_rows(wl.cu_seqlens, B)
+    pick = [allrows[i] for i in (0, 3, len(allrows) - 1, 7)]
+    sub = orc.compress(wl.q, wl.k, wl.cu_seqlens, B, 0.9, wl.bias(), rows=pick)
+    assert set(sub) == {(h, s, I) for h in range(2) for (s, I) in pick}
+    for key, rr in sub.items():
+        assert rr.kept == full[key].kept
+        assert np.array_equal(rr.P, full[key].P) and np.array_equal(rr.kmass, full[key].kmass)
+    out_full = orc.apply(full, wl.W, wl.v, wl.cu_seqlens, B, wl.spec.Hkv)
+    out_sub = orc.apply(full, wl.W, wl.v, wl.cu_seqlens, B, wl.spec.Hkv, rows=pick)
+    assert set(out_sub) == {(t, s, I) for t in range(3) for (s, I) in pick}
+    for key, o in out_sub.items():
+        assert np.array_equal(o, out_full[key])
 
 
 def test_shared_block_rows_compress_identically():
