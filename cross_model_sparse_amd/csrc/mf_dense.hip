@@ -12,16 +12,19 @@
 // each lane holding one query row, so the running max and sum (online softmax)
 // stay in the lane.  A row's running max moves only when a block's maximum
 // exceeds it by more than 8 (log2 units): the accumulated rows are rescaled
-// rarely, and P stays below 2^8.  P, rounded to bf16, is already in the
-// A-operand layout of the P V product, which runs on MFMA against the
-// transposed V tile.  No map is stored.
+// rarely, and P stays below 2^8 in the exact form (below 2^16 in the short
+// form below).  P, rounded to bf16, is already in the A-operand layout of the
+// P V product, which runs on MFMA against the transposed V tile.  No map is
+// stored.
 //
 // With bf16 inputs, Q is scaled by log2(e)/sqrt(d) once (one more bf16
-// rounding per element).  Blocks with one offset for all of their pairs then
-// take a short form: the Q K^T accumulators start from (offset - running max)
-// of the lane's row, so they leave the MFMA as exponents; P = exp2 of them,
-// with no per-block maximum, and the row sum is taken from the bf16 P.  A
-// block whose row sum passes 2^16 is redone in the exact form.
+// rounding per element).  Blocks with one offset for all of their pairs, and
+// blocks where only the local window's edge varies (its bias added per
+// element), then take a short form: the Q K^T accumulators start from
+// (offset - running max) of the lane's row, so they leave the MFMA as
+// exponents; P = exp2 of them, with no per-block maximum, and the row sum is
+// taken from the bf16 P.  A block whose row sum passes 2^16 is redone in the
+// exact form.
 #include <type_traits>
 
 #include "mf_host.hpp"
