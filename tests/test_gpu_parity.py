@@ -106,6 +106,17 @@ def test_zero_weight_row_and_no_renorm(gpu):
     assert float(O[1].abs().max()) == 0.0
 
 
+@pytest.mark.parametrize("idx,lens,kw,fmt", [
+    (2, [600, 77], dict(Hs=8, Ht=8, Hkv=8), "bf16"),   # eight sources per target: dense mixing
+    (4, [700], dict(Hs=8, Ht=16, Hkv=16), "mxfp8"),    # four sources per target, fp8 tiles
+    (2, [300, 45], dict(Hs=8, Ht=8, Hkv=4), "mxfp8"),  # dense mixing, fp8 tiles, GQA
+])
+def test_no_renorm_both_apply_kernels(gpu, idx, lens, kw, fmt):
+    """Raw kept maps (renormalisation off) through both apply kernels and both
+    tile formats."""
+    full_case(wlmod.small_variant(idx, lens, **kw), gpu, renorm=False, tile_format=fmt)
+
+
 def test_capacity_overflow_reported_and_bounded(gpu):
     """Capacity below the kept count: the status word says so, and nothing is written
     past the capacity (canary tiles and indices stay intact)."""
