@@ -117,6 +117,21 @@ def test_no_renorm_both_apply_kernels(gpu, idx, lens, kw, fmt):
     full_case(wlmod.small_variant(idx, lens, **kw), gpu, renorm=False, tile_format=fmt)
 
 
+def test_mixed_source_counts_and_partial_groups(gpu):
+    """Targets with more than four sources (dense mixing) next to targets with four
+    or fewer (sparse mixing) in one call; six targets, so the dense-mixing groups
+    of four end with a partial one."""
+    wl = wlmod.small_variant(2, [640, 200], Hs=8, Ht=6, Hkv=3)
+    W = wl.W.copy()
+    W[1, 2:] = 0.0                 # two sources
+    W[4, :] = 0.0
+    W[4, 5] = 0.7                  # one source
+    W[5, 4:] = 0.0                 # four sources
+    assert [int((W[t] != 0).sum()) for t in range(6)] == [8, 2, 8, 8, 1, 4]
+    full_case(wl, gpu, W=W)
+    full_case(wl, gpu, W=W, tile_format="mxfp8")
+
+
 def test_capacity_overflow_reported_and_bounded(gpu):
     """Capacity below the kept count: the status word says so, and nothing is written
     past the capacity (canary tiles and indices stay intact)."""
