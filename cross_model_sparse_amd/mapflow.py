@@ -138,6 +138,23 @@ def _dev_cu(cu_host: np.ndarray, device) -> torch.Tensor:
     return torch.from_numpy(cu_host).to(device)
 
 
+def _check_tokens(what: str, t: torch.Tensor, cu: np.ndarray):
+    """The kernels use cu_seqlens[-1] as the token count of every [H, T, d]
+    tensor (its head stride); a tensor of another length would be read or
+    written at the wrong offsets."""
+    if len(cu) == 0:
+        raise ValueError("cu_seqlens must have at least one entry")
+    if t.dim() != 3 or int(t.shape[1]) != int(cu[-1]):
+        raise ValueError(f"{what} must be [H, T, d] with T = cu_seqlens[-1] = {int(cu[-1])}, "
+                         f"got {tuple(t.shape)}")
+
+
+def _check_out(out: torch.Tensor, shape, dtype=torch.float32):
+    if out.dtype != dtype or tuple(out.shape) != tuple(shape) or not out.is_contiguous():
+        raise ValueError(f"out must be contiguous {dtype} {tuple(shape)}, got {out.dtype} "
+                         f"{tuple(out.shape)}")
+
+
 # ---------------------------------------------------------------------------
 # size queries
 # ---------------------------------------------------------------------------
@@ -243,6 +260,7 @@ def mf_prefix_dedupe(q: torch.Tensor, k: torch.Tensor, cu_seqlens, B: int,
     Hs, T, d = q.shape
     if k.shape != q.shape or k.dtype != q.dtype or not (q.is_contiguous() and k.is_contiguous()):
         raise ValueError("q and k must be contiguous, of the same shape and dtype")
+    _check_tokens("q", q, cu)
     dev = q.device
     nbr = mf_num_block_rows(cu, B)
     if nbr < 0:
@@ -278,6 +296,7 @@ def mf_compress_topp(q: torch.Tensor, k: torch.Tensor, cu_seqlens, B: int, p: fl
         raise ValueError("q and k must have the same shape and dtype")
     if not (q.is_contiguous() and k.is_contiguous()):
         raise ValueError("q and k must be contiguous")
+    _check_tokens("q", q, cu)
     dev = q.device
     m = out if out is not None else alloc_map(Hs, cu, B, dev, capacity, tile_format)
     if row_alias is not None and (row_alias.dtype != torch.int32 or not row_alias.is_contiguous()):
@@ -314,11 +333,14 @@ def mf_apply_translated(m: BsrMap, W: torch.Tensor, v: torch.Tensor, cu_seqlens,
     Hkv, T, d = v.shape
     if v.dtype != torch.bfloat16 or not v.is_contiguous():
         raise ValueError("v must be contiguous bfloat16")
-    if W.dtype != torch.float32 or not W.is_contiguous() or W.shape[1] != m.num_heads:
+    if W.dtype != torch.float32 or not W.is_contiguous() or W.dim() != 2 or W.shape[1] != m.num_heads:
         raise ValueError("W must be contiguous float32 [Ht, Hs]")
+    _check_tokens("v", v, cu)
     dev = v.device
     if out is None:
         out = torch.empty((Ht, T, d), dtype=torch.float32, device=dev)
+    else:
+        _check_out(out, (Ht, T, d))
     if workspace is None:
         workspace = torch.empty(mf_apply_workspace_bytes(Hkv, cu, m.block, d), dtype=torch.uint8, device=dev)
     if cu_dev is None:
@@ -348,12 +370,14 @@ def mf_apply_translated_paged(m: BsrMap, W: torch.Tensor, pages: torch.Tensor, b
         raise ValueError("pages must be contiguous bfloat16 [num_pages, Hkv, page_size, d]")
     if block_table.dtype != torch.int32 or not block_table.is_contiguous() or block_table.dim() != 2:
         raise ValueError("block_table must be contiguous int32 [nseq, max_pages]")
-    if W.dtype != torch.float32 or not W.is_contiguous() or W.shape[1] != m.num_heads:
+    if W.dtype != torch.float32 or not W.is_contiguous() or W.dim() != 2 or W.shape[1] != m.num_heads:
         raise ValueError("W must be contiguous float32 [Ht, Hs]")
     dev = pages.device
     T = int(cu[-1])
     if out is None:
         out = torch.zeros((Ht, T, d), dtype=torch.float32, device=dev)
+    else:
+        _check_out(out, (Ht, T, d))
     if workspace is None:
         workspace = torch.empty(mf_apply_workspace_bytes(Hkv, cu, m.block, d), dtype=torch.uint8, device=dev)
     if cu_dev is None:
@@ -387,9 +411,12 @@ def mf_tv_distance(m: BsrMap, W: torch.Tensor, q: torch.Tensor, k: torch.Tensor,
         raise ValueError("q and k must be contiguous, of one dtype, [H, T, d]")
     if W.dtype != torch.float32 or not W.is_contiguous() or tuple(W.shape) != (Ht, m.num_heads):
         raise ValueError("W must be contiguous float32 [Ht, Hs]")
+    _check_tokens("q", q, cu)
     dev = q.device
     if out is None:
         out = torch.empty((Ht, T), dtype=torch.float32, device=dev)
+    else:
+        _check_out(out, (Ht, T))
     if workspace is None:
         workspace = torch.empty(lib.mf_tv_distance_workspace_bytes(_cu_ptr(cu), len(cu) - 1, m.block),
                                 dtype=torch.uint8, device=dev)
@@ -415,9 +442,16 @@ def mf_dense_ref_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu
     Hkv = k.shape[0]
     if k.dtype != q.dtype or v.dtype != torch.bfloat16:
         raise ValueError("k must match q's dtype; v must be bfloat16")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k and v must be contiguous")
+    if k.dim() != 3 or tuple(k.shape[1:]) != (T, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must be [Hkv, T, d] with q's T and d")
+    _check_tokens("q", q, cu)
     dev = q.device
     if out is None:
         out = torch.empty((Hq, T, d), dtype=torch.float32, device=dev)
+    else:
+        _check_out(out, (Hq, T, d))
     if workspace is None:
         workspace = torch.empty(mf_dense_workspace_bytes(Hkv, cu, d), dtype=torch.uint8, device=dev)
     if cu_dev is None:

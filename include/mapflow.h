@@ -244,7 +244,8 @@ size_t mf_apply_workspace_bytes(int32_t Hkv, const int32_t *cu_seqlens_host, int
  *              (A_hat_h[i,j] / kept_mass_h[i]) V_g(t)[j,:],   g(t) = t / (Ht / Hkv)
  * With renorm == 0 the division by kept mass is dropped.  A row whose kept
  * mass is 0 contributes nothing.  W = identity gives per-head reuse of the
- * cached map (AttnCache guide, "Output = A_c @ V").
+ * cached map: O_h = renorm(A_hat_h) V_h (AttnCache guide, architecture
+ * figure, cache-hit path).
  *
  * map         host struct filled by mf_compress_topp; read only.
  * W           [Ht][map->num_heads] fp32, any sign; zero entries are skipped.
