@@ -27,8 +27,22 @@ namespace mf {
 constexpr int kXcds = 8;
 constexpr int kBufferFlags = 0x00020000;  // buffer descriptor word 3 for raw dword loads
 
+// A wave-uniform value the compiler cannot prove uniform (it was loaded from
+// memory, or computed from such a load), moved to a scalar register so buffer
+// descriptors built from it need no per-lane loop.
+__device__ __forceinline__ int uni32(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int64_t uni64(int64_t x) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // ---------------------------------------------------------------------------
-// V -> Vt [Hkv][D][NBR * B], zero past each sequence end.
+// V -> Vs [Hkv][NBR * B / 16][D][16]: each sequence block-padded to whole key
+// blocks, cut into 16-key chunks, and each chunk stored head dimension major
+// (column d holds its 16 keys as 32 contiguous bytes).  One chunk of one head
+// is then D * 32 contiguous bytes, and 8 consecutive keys of one value column
+// (an MFMA B operand) are one 16-byte piece.  Keys past a sequence end are zero.
 //
 // V is either contiguous [Hkv][T][D] or paged: token j of sequence s lives in
 // page block_table[s][j / P] of a pool [pages][Hkv][P][D] at slot j % P (page
@@ -43,10 +57,15 @@ struct VSrc {
   const int32_t *window;      // [nseq][2] query tokens [begin, end), or null
 };
 
+// element offset of (head g, global padded key column col, value column d) in Vs
+__device__ __forceinline__ int64_t vs_index(int64_t NBR, int B, int D, int g, int64_t col, int d) {
+  return (((int64_t)g * NBR * B + (col & ~int64_t(15))) * D) + (int64_t)d * 16 + (col & 15);
+}
+
 template <int B, int D>
-__global__ __launch_bounds__(256) void k_vtranspose(VSrc vs, int64_t T,
-                                                    const RowInfo *__restrict__ rows, int32_t NBR,
-                                                    uint16_t *__restrict__ vt) {
+__global__ __launch_bounds__(256) void k_vstage(VSrc vs, int64_t T,
+                                                const RowInfo *__restrict__ rows, int32_t NBR,
+                                                uint16_t *__restrict__ vt) {
   constexpr int P = B + 8;  // LDS row pitch in elements
   __shared__ __attribute__((aligned(16))) uint16_t t[D * P];
   const int gr = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
@@ -76,12 +95,13 @@ __global__ __launch_bounds__(256) void k_vtranspose(VSrc vs, int64_t T,
     }
   }
   __syncthreads();
-  const int64_t tpad = (int64_t)NBR * B;
-  uint16_t *dst = vt + (int64_t)g * D * tpad + (int64_t)gr * B;
-  for (int idx = tid; idx < D * B / 8; idx += 256) {
-    const int d = idx / (B / 8), c = idx % (B / 8);
-    *reinterpret_cast<u32x4 *>(dst + (int64_t)d * tpad + c * 8) =
-        *reinterpret_cast<const u32x4 *>(&t[d * P + c * 8]);
+  // the block's B / 16 chunks are B * D contiguous elements; 16-byte piece
+  // (chunk, d, half) at ((chunk * D + d) * 2 + half) * 8
+  uint16_t *dst = vt + vs_index(NBR, B, D, g, (int64_t)gr * B, 0);
+  for (int idx = tid; idx < B * D / 8; idx += 256) {
+    const int half = idx & 1, d = (idx >> 1) % D, ch = (idx >> 1) / D;
+    *reinterpret_cast<u32x4 *>(dst + (int64_t)idx * 8) =
+        *reinterpret_cast<const u32x4 *>(&t[d * P + ch * 16 + half * 8]);
   }
 }
 
@@ -335,31 +355,34 @@ __device__ __forceinline__ void mix_word(float &even, float &odd, uint32_t w, ui
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// One 16-byte piece per lane, memory -> LDS: the wave's 64 pieces land at
+// lds + 16 * lane.
+template <int AUX>
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, char *lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, voff, soff, 0, AUX);
+}
+
 // V tile of key block J -> LDS buffer with direct buffer->LDS loads (the same
 // load class as the tile reads, so the compiler's wait counts stay exact); the
-// wave moves VINST 1 KB blocks.  16-byte chunk c of row d is stored at chunk
-// position c ^ (d % CPR), so the MFMA B-operand reads below are conflict-free.
+// wave moves VINST 1 KB blocks.  In LDS, row d of the tile (B keys) holds its
+// 16-byte pieces c (keys 8c .. 8c + 7) at position c ^ (d % CPR), so the MFMA
+// B-operand reads below are conflict-free.  In the staged V (k_vstage) the tile
+// is B * D contiguous elements, piece (d, c) at ((c / 2) * D + d) * 16 + (c % 2) * 8.
 template <int B, int D, int VINST>
-__device__ __forceinline__ void dma_v_tile(char *dstbuf, const uint16_t *vtg, int64_t tpad,
-                                           int64_t col0, int wave, int lane) {
-  constexpr int CPR = B * 2 / 16;   // 16-byte chunks per row
+__device__ __forceinline__ void dma_v_tile(char *dstbuf, const uint16_t *vtg, int64_t col0,
+                                           int wave, int lane) {
+  constexpr int CPR = B * 2 / 16;   // 16-byte pieces per row
   constexpr int RPB = 64 / CPR;     // rows per 1 KB block
-  // the swizzle of a block's rows repeats every PER blocks: the lane part of
-  // the offset takes PER values, the row part d0 * tpad * 2 is uniform
-  constexpr int PER = CPR * CPR / 64 > 1 ? CPR * CPR / 64 : 1;
-  // one descriptor per tile; byte offsets d * tpad * 2 stay below 2^31 (checked
-  // by the host)
-  const __amdgpu_buffer_rsrc_t r =
-      __builtin_amdgcn_make_buffer_rsrc((void *)(vtg + col0), 0, 0x7fffffff, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(vtg + col0 * D), 0, B * D * 2, kBufferFlags);
   const int dl = lane / CPR, pp = lane % CPR;
 #pragma unroll
   for (int i = 0; i < VINST; ++i) {
     const int blk = wave * VINST + i;        // 1 KB block of the tile
     const int d0 = blk * RPB;                // its first row
-    const int c = pp ^ ((d0 + dl) % CPR);    // swizzled chunk position
-    (void)PER;
-    const int voff = (dl * (int)tpad + c * 8) * 2;
-    const int soff = d0 * (int)tpad * 2;
+    const int c = pp ^ ((d0 + dl) % CPR);    // swizzled piece position
+    const int voff = (((c >> 1) * D + dl) * 16 + (c & 1) * 8) * 2;
+    const int soff = d0 * 32;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dstbuf + blk * 1024), 16, voff, soff, 0, 0);
   }
 }
@@ -525,7 +548,7 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(4))) void
 
   const uint16_t *vtg = vt + (int64_t)g * D * tpad;
   auto dma_v = [&](char *dstbuf, int J) {
-    dma_v_tile<B, D, C::VINST>(dstbuf, vtg, tpad, (int64_t)(gr - I + J) * B, wave, lane);
+    dma_v_tile<B, D, C::VINST>(dstbuf, vtg, (int64_t)(gr - I + J) * B, wave, lane);
   };
 
   f32x4 acc[RG][D / 16];
@@ -688,8 +711,6 @@ struct ApplyMixCfg {
   static_assert(VINST * 1024 * NW == VBYTES, "V tile must split into 1 KB wave loads");
   static_assert(G * VBYTES <= 64 * 1024, "V buffers must stay in the first 64 KB of LDS");
 };
-constexpr int kMixMaxSources = 128;
-
 // Dynamic LDS of k_apply_mix (byte offsets): src[Hs] int32, rbase[Hs] int64,
 // wtab[Hs][4] fp32 (weight of each source for each target of the group),
 // bm[Hs][nbw], pc[Hs][nbw], uni[nbw], rtab[Hs][B] fp32 (1 / kept mass of each
@@ -895,8 +916,8 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(2))) void
     // V tiles of this block for every distinct V head of the group
     const int64_t col0 = (int64_t)(gr - I + J) * B;
     for (int vh = 0; vh < nvh; ++vh)
-      dma_v_tile<B, D, C::VINST>(vbuf + vh * C::VBYTES, vt + (int64_t)(gv0 + vh) * D * tpad, tpad,
-                                 col0, wave, lane);
+      dma_v_tile<B, D, C::VINST>(vbuf + vh * C::VBYTES, vt + (int64_t)(gv0 + vh) * D * tpad, col0,
+                                 wave, lane);
 
     u32x4 amix[G];
     // Buffer loads through one descriptor per source (wave-uniform base, 32-bit
@@ -1029,31 +1050,620 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(2))) void
   }
 }
 
-// The two apply kernels for one tile format, over `nrows` block-rows of `sched`.
+// ---------------------------------------------------------------------------
+// Target pairs for k_apply_pair.
+//
+// Targets with at most four sources are paired so that one work-group loads
+// each source tile of both once and mixes it into whichever of the two uses
+// it.  Greedy and deterministic: the lowest-numbered target not yet placed
+// takes the unplaced target whose sources add the fewest new ones (lowest
+// number on ties).  Any two such targets fit (at most 8 sources).  Targets with
+// more than four sources are left to k_apply_mix.
+//
+// gtab[0] = number of pairs; pair q holds targets gtab[1 + 2q], gtab[2 + 2q]
+// (-1 for an empty slot).  One wave; Ht <= kMaxTargets, Hs <= kMixMaxSources.
+// ---------------------------------------------------------------------------
+constexpr int kPairT = 2;          // targets per work-group
+constexpr int kPairU = 8;          // sources of a work-group (their union)
+constexpr int kMaxTargets = 1024;
+constexpr int kMixMaxSources = 128;
+
+__global__ __launch_bounds__(64) void k_pairs(const float *__restrict__ W, int32_t Ht, int32_t Hs,
+                                              int32_t *__restrict__ gtab) {
+  __shared__ uint32_t msk[kMaxTargets][4];
+  __shared__ uint8_t state[kMaxTargets];  // 0 free, 1 placed, 2 not handled here
+  const int lane = threadIdx.x;
+  for (int t = lane; t < Ht; t += 64) {
+    uint32_t m[4] = {0u, 0u, 0u, 0u};
+    for (int h = 0; h < Hs; ++h)
+      if (W[(int64_t)t * Hs + h] != 0.f) m[h >> 5] |= 1u << (h & 31);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) msk[t][w] = m[w];
+    const int cnt = __popc(m[0]) + __popc(m[1]) + __popc(m[2]) + __popc(m[3]);
+    state[t] = cnt <= 4 ? 0 : 2;
+  }
+  __syncthreads();
+  auto wave_min = [](int v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
+    return v;
+  };
+  int np = 0;
+  for (;;) {
+    int first = INT32_MAX;
+    for (int t = lane; t < Ht; t += 64)
+      if (state[t] == 0) first = min(first, t);
+    first = wave_min(first);
+    if (first == INT32_MAX) break;
+    __syncthreads();
+    if (lane == 0) state[first] = 1;
+    __syncthreads();
+    int best = INT32_MAX;
+    for (int t = lane; t < Ht; t += 64) {
+      if (state[t] != 0) continue;
+      int nu = 0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) nu += __popc(msk[first][w] | msk[t][w]);
+      best = min(best, nu * kMaxTargets + t);
+    }
+    best = wave_min(best);
+    const int second = best == INT32_MAX ? -1 : best % kMaxTargets;
+    __syncthreads();
+    if (lane == 0 && second >= 0) state[second] = 1;
+    if (lane == 0) {
+      gtab[1 + 2 * np] = first;
+      gtab[2 + 2 * np] = second;
+    }
+    __syncthreads();
+    ++np;
+  }
+  if (lane == 0) gtab[0] = np;
+}
+
+// ---------------------------------------------------------------------------
+// Query-block pairs: block-rows I and I - 1 of one sequence, counted from the
+// last block-row of the sequence (or of its query window) down, so a sequence
+// with an odd number of block-rows ends in a single one.  Listed lead block
+// (the longer) descending, from the longest-first schedule; psched[2p] is the
+// lead's global block-row, psched[2p + 1] the partner's or -1.  One work-group.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void k_pair_sched(const RowInfo *__restrict__ rows,
+                                                     const int32_t *__restrict__ sched,
+                                                     int32_t NBR, int32_t B,
+                                                     const int32_t *__restrict__ window,
+                                                     int32_t *__restrict__ psched) {
+  __shared__ int32_t wsum[16];
+  __shared__ int32_t base;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) base = 0;
+  __syncthreads();
+  for (int p0 = 0; p0 < NBR; p0 += 1024) {
+    const int p = p0 + tid;
+    int gr = -1, partner = -1;
+    bool lead = false;
+    if (p < NBR) {
+      gr = sched[p];
+      const RowInfo ri = rows[gr];
+      int lo = 0, hi = (ri.len + B - 1) / B - 1;  // block-rows of the sequence (or window)
+      if (window) {
+        const int a = window[2 * ri.seq], e = window[2 * ri.seq + 1];
+        lo = a / B;
+        hi = (e + B - 1) / B - 1;
+      }
+      if (ri.blk >= lo && ri.blk <= hi) {
+        lead = ((hi - ri.blk) & 1) == 0;
+        partner = ri.blk - 1 >= lo ? gr - 1 : -1;
+      }
+    }
+    const uint64_t mask = wave_ballot(lead);
+    if (lane == 0) wsum[wave] = __popcll(mask);
+    __syncthreads();
+    int off = base;
+    for (int w = 0; w < wave; ++w) off += wsum[w];
+    if (lead) {
+      const int q = off + lanes_below(mask);
+      psched[2 * q] = gr;
+      psched[2 * q + 1] = partner;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int tot = 0;
+      for (int w = 0; w < 16; ++w) tot += wsum[w];
+      base += tot;
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// k_apply_pair: targets with at most four sources, one work-group per (query
+// block pair, target pair).
+//
+// The work-group covers 2B rows (two adjacent query blocks of one sequence)
+// for two targets.  Per 16-key step of each key block in the union of the
+// kept sets (both query blocks, every source of either target), it stages in
+// LDS, once: each source's slice of both query blocks' tiles (2B rows x 16
+// keys) and each target's V slice (16 keys x D, one V for both query blocks:
+// they are of one sequence).  Wave (a, part) rebuilds 64 rows of target a's
+// translated tile from its (at most four) sources,
+//   A~_a[i, j] = sum_b c_ab[i] A_src(a,b)[i, j],   c_ab[i] = W[t_a, h] / kmass_h[i],
+// in fp32 (bf16 values widened exactly, fp32 coefficients, fp32 fused
+// multiply-adds), rounds it to bf16 once and multiplies it with V on 32x32x16
+// MFMAs into fp32 accumulators; each V operand read serves two 32-row blocks.
+// The translated map never leaves registers.
+//
+// Loads: per key block, each wave builds one buffer descriptor per source
+// piece (a tile of one query block, zero-length where the source kept no tile)
+// and per V piece; steps inside the block only move the scalar offset.  The
+// loads of step q + 2 go to a register stage while step q is computed from one
+// LDS stage and step q + 1 moves to the other; one barrier per step.  Every
+// lane issues the same number of loads every step, so wait counts are exact.
+//
+// Order: consecutive work-group ids go to the XCDs in turn.  One XCD runs all
+// target pairs of one query-block pair at a time (32 work-groups for 64
+// targets), so they start together and read each shared source tile from that
+// XCD's L2.  The key blocks are walked upwards or downwards by the lead block's
+// index (I / 16 odd: downwards), so the query blocks in flight on all XCDs,
+// which start in rounds of 16 longest-first, stay close in J and share V
+// through the memory-side cache.
+// ---------------------------------------------------------------------------
+constexpr int kPairVPolicy = 0;    // cache policy of the V loads
+
+template <int B, int D>
+struct PairCfg {
+  static constexpr int ROWS = 2 * B;                    // rows of a work-group
+  static constexpr int WPT = ROWS >= 128 ? ROWS / 64 : 1;   // waves per target
+  static constexpr int NW = kPairT * WPT;
+  static constexpr int NT = NW * 64;
+  static constexpr int RB = ROWS / (32 * WPT);          // 32-row blocks per wave
+  static constexpr int NB = D / 32;                     // 32-column blocks
+  static constexpr int KS = B / 16;                     // 16-key steps per key block
+  static constexpr int SRC_BYTES = ROWS * 32;           // a source's slice of one step
+  static constexpr int V_BYTES = D * 32;                // a target's V slice of one step
+  static constexpr int V_OFF = kPairU * SRC_BYTES;
+  static constexpr int STAGE = V_OFF + kPairT * V_BYTES;
+  static constexpr int SP = kPairU * SRC_BYTES / 16 / NT;               // source pieces per lane
+  static constexpr int VPIECES = kPairT * V_BYTES / 16;
+  static constexpr int VP = (VPIECES + NT - 1) / NT;                    // V pieces per lane
+  static constexpr int NP = SP + VP;
+  static_assert(2 * ROWS == NT, "a lane's source pieces are one per slot");
+  static_assert(RB == 2 && (2 * D) % 64 == 0 && KS % 2 == 0, "layout assumptions");
+};
+
+// LDS tables after the two stages (byte offsets)
+struct PairTables {
+  int rbase, rend, usrc, smap, sw, sns, stgt, umask, misc, bm, pc, uni, upre, blist, total;
+};
+template <int B, int D>
+__host__ __device__ inline PairTables pair_tables(int nbw) {
+  using C = PairCfg<B, D>;
+  PairTables t;
+  int o = 2 * C::STAGE;
+  t.rbase = o; o += 2 * kPairU * 8;
+  t.rend = o; o += 2 * kPairU * 8;
+  t.usrc = o; o += kPairU * 4;
+  t.smap = o; o += 8 * 4;
+  t.sw = o; o += 8 * 4;
+  t.sns = o; o += 4 * 4;
+  t.stgt = o; o += 4 * 4;
+  t.umask = o; o += 4 * 4;
+  t.misc = o; o += 4 * 4;
+  t.bm = o; o += 2 * kPairU * nbw * 4;
+  t.pc = o; o += 2 * kPairU * nbw * 4;
+  t.uni = o; o += nbw * 4;
+  t.upre = o; o += nbw * 4;
+  t.blist = o; o += nbw * 32 * 4;
+  t.total = o;
+  return t;
+}
+
+template <int B, int D>
+__global__ __launch_bounds__((PairCfg<B, D>::NT)) __attribute__((amdgpu_waves_per_eu(2)))
+void k_apply_pair(const int64_t *__restrict__ row_ptr, const int32_t *__restrict__ col_idx,
+                  const char *__restrict__ tiles, const float *__restrict__ kept_mass, int32_t Hs,
+                  int32_t NBR, int64_t T, const float *__restrict__ W, int32_t grp,
+                  const uint16_t *__restrict__ vt, const RowInfo *__restrict__ rows,
+                  const int32_t *__restrict__ psched, int32_t npairs, int32_t nbw,
+                  int64_t capacity, int32_t renorm, float *__restrict__ o,
+                  const int32_t *__restrict__ row_alias, const int32_t *__restrict__ gtab,
+                  int32_t ngmax) {
+  using C = PairCfg<B, D>;
+  constexpr int RB = C::RB, NB = C::NB, KS = C::KS, SP = C::SP, VP = C::VP, NP = C::NP;
+  constexpr int64_t TBYTES = (int64_t)B * B * 2;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const PairTables tb = pair_tables<B, D>(nbw);
+  int64_t *rbase = reinterpret_cast<int64_t *>(smem + tb.rbase);  // [2][U] first tile of the row
+  int64_t *rend = reinterpret_cast<int64_t *>(smem + tb.rend);    // [2][U] end (capped)
+  int32_t *usrc = reinterpret_cast<int32_t *>(smem + tb.usrc);    // [U] source head
+  int32_t *smap = reinterpret_cast<int32_t *>(smem + tb.smap);    // [2][4] slot of source b of target a
+  float *sw = reinterpret_cast<float *>(smem + tb.sw);            // [2][4] weight
+  int32_t *sns = reinterpret_cast<int32_t *>(smem + tb.sns);      // [2] source count
+  int32_t *stgt = reinterpret_cast<int32_t *>(smem + tb.stgt);    // [2] target or -1
+  uint32_t *umask = reinterpret_cast<uint32_t *>(smem + tb.umask);
+  int32_t *misc = reinterpret_cast<int32_t *>(smem + tb.misc);    // [0] union blocks
+  uint32_t *bm = reinterpret_cast<uint32_t *>(smem + tb.bm);      // [2][U][nbw] kept bitmaps
+  int32_t *pc = reinterpret_cast<int32_t *>(smem + tb.pc);        // [2][U][nbw] popcount prefix
+  uint32_t *uni = reinterpret_cast<uint32_t *>(smem + tb.uni);
+  int32_t *upre = reinterpret_cast<int32_t *>(smem + tb.upre);
+  int32_t *blist = reinterpret_cast<int32_t *>(smem + tb.blist);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // work-group -> (query-block pair, target pair)
+  const int x = blockIdx.x % kXcds, kx = blockIdx.x / kXcds;
+  const int round = kx / ngmax, gi = kx % ngmax;
+  const int pidx = round * kXcds + ((round & 1) ? (kXcds - 1 - x) : x);
+  if (pidx >= npairs) return;
+  if (gi >= gtab[0]) return;
+  int grq[2], Iq[2], grmq[2];
+  grq[0] = uni32(psched[2 * pidx]);
+  grq[1] = uni32(psched[2 * pidx + 1]);
+  const RowInfo r0 = rows[grq[0]];
+  const int L = uni32(r0.len);
+  const int64_t tok0 = (int64_t)uni32(r0.start);
+  Iq[0] = uni32(r0.blk);
+  Iq[1] = Iq[0] - 1;                                   // partner (if any) is the block below
+  const bool has1 = grq[1] >= 0;
+  const int grow0 = grq[0] - Iq[0];                    // the sequence's first global block-row
+  const int n = Iq[0] + 1;                             // key blocks J <= I of the lead
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int g = b == 0 ? grq[0] : (has1 ? grq[1] : grq[0]);
+    const int ga = row_alias ? uni32(row_alias[g]) : g;
+    grmq[b] = (ga >= 0 && ga < NBR) ? ga : g;
+  }
+  const bool desc = ((Iq[0] >> 4) & 1) != 0;
+
+  // ---- set-up: targets, their sources, the source union -------------------
+  if (tid < 4) umask[tid] = 0u;
+  if (tid < kPairT) stgt[tid] = gtab[1 + 2 * gi + tid];
+  for (int i = tid; i < 2 * kPairU * nbw; i += C::NT) bm[i] = 0u;
+  __syncthreads();
+  if (wave < kPairT) {
+    const int t = stgt[wave];
+    int ns = 0;
+    if (t >= 0)
+      for (int h0 = 0; h0 < Hs; h0 += 64) {
+        const int h = h0 + lane;
+        const float w = h < Hs ? W[(int64_t)t * Hs + h] : 0.f;
+        const uint64_t mask = wave_ballot(w != 0.f);
+        if (w != 0.f) {
+          const int q = ns + lanes_below(mask);
+          if (q < 4) {
+            smap[wave * 4 + q] = h;   // head for now, slot below
+            sw[wave * 4 + q] = w;
+          }
+          atomicOr(&umask[h >> 5], 1u << (h & 31));
+        }
+        ns += __popcll(mask);
+      }
+    if (lane == 0) sns[wave] = min(ns, 4);
+  }
+  __syncthreads();
+  const uint32_t um0 = umask[0], um1 = umask[1], um2 = umask[2], um3 = umask[3];
+  auto slot_of = [&](int h) {  // rank of head h in the union
+    const uint32_t below = (h & 31) ? ((1u << (h & 31)) - 1u) : 0u;
+    const int w = h >> 5;
+    int r = __popc((w == 0 ? um0 : w == 1 ? um1 : w == 2 ? um2 : um3) & below);
+    if (w > 0) r += __popc(um0);
+    if (w > 1) r += __popc(um1);
+    if (w > 2) r += __popc(um2);
+    return r;
+  };
+  const int U = __popc(um0) + __popc(um1) + __popc(um2) + __popc(um3);  // <= kPairU
+  if (tid < kMixMaxSources) {
+    const int h = tid;
+    if ((umask[h >> 5] >> (h & 31)) & 1u) {
+      const int u = slot_of(h);
+      usrc[u] = h;
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const bool on = b == 0 || has1;
+        rbase[b * kPairU + u] = on ? row_ptr[(int64_t)h * NBR + grmq[b]] : 0;
+        rend[b * kPairU + u] = on ? min(row_ptr[(int64_t)h * NBR + grmq[b] + 1], capacity) : 0;
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < 8) {
+    const int a = tid >> 2, b = tid & 3;
+    smap[tid] = b < sns[a] ? slot_of(smap[tid]) : 0;
+  }
+  // kept bitmaps of the union's sources, both query blocks
+  for (int bu = 0; bu < 2 * U; ++bu) {
+    const int b = bu / U, u = bu % U;
+    const int64_t e = rend[b * kPairU + u];
+    for (int64_t idx = rbase[b * kPairU + u] + tid; idx < e; idx += C::NT) {
+      const int J = col_idx[idx];
+      atomicOr(&bm[(b * kPairU + u) * nbw + (J >> 5)], 1u << (J & 31));
+    }
+  }
+  __syncthreads();
+  const int nw_row = (n + 31) / 32;
+  for (int i = tid; i < 2 * kPairU * nw_row; i += C::NT) {
+    // popcount prefix of each bitmap (its tile rank before word w)
+    const int bu = i / nw_row, w = i % nw_row;
+    int run = 0;
+    for (int v = 0; v < w; ++v) run += __popc(bm[bu * nbw + v]);
+    pc[bu * nbw + w] = run;
+  }
+  if (tid < nw_row) {
+    uint32_t v = 0u;
+    for (int bu = 0; bu < 2 * kPairU; ++bu) v |= bm[bu * nbw + tid];
+    uni[tid] = v;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int w = 0; w < nw_row; ++w) {
+      upre[w] = run;
+      run += __popc(uni[w]);
+    }
+    misc[0] = run;
+  }
+  __syncthreads();
+  const int nblk = uni32(misc[0]);
+  for (int J = tid; J < n; J += C::NT) {
+    const uint32_t w = uni[J >> 5];
+    if ((w >> (J & 31)) & 1u) blist[upre[J >> 5] + __popc(w & ((1u << (J & 31)) - 1u))] = J;
+  }
+  __syncthreads();
+
+  // ---- per-wave constants ---------------------------------------------------
+  const int a = wave % kPairT, part = wave / kPairT;    // target slot, 64-row part
+  const int ta = uni32(stgt[a]);
+  const int nsa = uni32(sns[a]);
+  const int r32 = lane & 31;
+  // coefficients c[rb][b] of the lane's rows (zero past the sequence end, for
+  // absent sources and where the kept mass is 0)
+  float cf[RB][4];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int row = 64 * part + 32 * rb + r32;           // row of the work-group
+    const int q = row / B;                               // its query block
+    const int ip = Iq[q] * B + row % B;                  // row inside the sequence
+    const bool live = q == 0 || has1;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      float c = 0.f;
+      if (ta >= 0 && live && b < nsa && ip < L) {
+        const int h = usrc[smap[a * 4 + b]];
+        const float w = sw[a * 4 + b];
+        if (renorm) {
+          const float km = kept_mass[(int64_t)h * T + tok0 + ip];
+          c = km > 0.f ? w / km : 0.f;
+        } else {
+          c = w;
+        }
+      }
+      cf[rb][b] = c;
+    }
+  }
+  int soff_b[4];  // LDS offset of the slot of each source of target a (uniform)
+#pragma unroll
+  for (int b = 0; b < 4; ++b) soff_b[b] = uni32(smap[a * 4 + b]) * C::SRC_BYTES;
+  // LDS layouts are lane-linear, so every read and write of a wave covers
+  // contiguous bytes (no bank conflicts): a source slice is ROWS/32 blocks of
+  // 1 KB, block k holding (key half h, row r of the block) at (32 h + r) * 16,
+  // the A operand of a 32x32x16 MFMA for lane 32 h + r; a V slice is D/32
+  // blocks of 1 KB, block nb holding (key half h, column d of the block) at
+  // (32 h + d) * 16, the B operand for lane 32 h + d.
+  int aoff[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) aoff[rb] = (2 * part + rb) * 1024 + lane * 16;
+  const int boff = C::V_OFF + a * C::V_BYTES + lane * 16;
+
+  // load pieces, moved straight from memory to LDS (each load instruction of a
+  // wave fills 64 consecutive 16-byte LDS positions).  Source piece i of a
+  // lane: slot i, position tid of the slot, in query block qw (uniform per
+  // wave).  V piece j: target slot v_slot[j] (uniform), position r of its slice.
+  const int srow = 32 * (tid >> 6) + (tid & 31), shalf = (tid >> 5) & 1;
+  const int qw = uni32(srow / B);                      // query block of this wave's source pieces
+  const int srow_in = srow % B;
+  const int p_goff = (srow_in >> 4) * (B / 32) * 1024 + (shalf * 16 + (srow_in & 15)) * 16;
+  const int p_lds = wave * 1024;                       // the wave's block inside a slot
+  int v_slot[VP], v_goff[VP], v_lds[VP];
+#pragma unroll
+  for (int j = 0; j < VP; ++j) {
+    const int p = tid + C::NT * j;
+    v_slot[j] = uni32(p / (2 * D));
+    const int r = p % (2 * D);
+    const int d = 32 * (r >> 6) + (r & 31), half = (r >> 5) & 1;
+    v_goff[j] = (d * 2 + half) * 16;                   // staged V chunk: column d, key half
+    v_lds[j] = uni32(C::V_OFF + v_slot[j] * C::V_BYTES + (r - lane) * 16);
+  }
+  int v_head[VP];  // V head of each V piece's target (-1: no target, or past the slices)
+#pragma unroll
+  for (int j = 0; j < VP; ++j) {
+    const int t = v_slot[j] < kPairT ? uni32(stgt[v_slot[j]]) : -1;
+    v_head[j] = t >= 0 ? t / grp : -1;
+  }
+  const int64_t vhead_elems = (int64_t)NBR * B * D;
+  const int nsteps = nblk * KS;
+
+  // per key block: descriptors of the tiles of the wave's source pieces (slot
+  // i of query block qw) and of the V block of its V pieces
+  struct Desc {
+    __amdgpu_buffer_rsrc_t t[SP];
+    __amdgpu_buffer_rsrc_t v[VP];
+  };
+  auto make_desc = [&](Desc &dd, int k) {
+    const bool valid = k < nblk;
+    const int kk = valid ? (desc ? nblk - 1 - k : k) : 0;
+    const int J = uni32(blist[kk]);
+    // lane i < U: tile index of slot i of query block qw at J, or -1
+    int ti = -1;
+    if (valid && lane < U && (qw == 0 || has1)) {
+      const int bu = qw * kPairU + lane;
+      const uint32_t wd = bm[bu * nbw + (J >> 5)];
+      if ((wd >> (J & 31)) & 1u) {
+        const int64_t x = rbase[bu] + pc[bu * nbw + (J >> 5)] + __popc(wd & ((1u << (J & 31)) - 1u));
+        if (x < rend[bu]) ti = (int)x;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < SP; ++i) {
+      const int tix = __builtin_amdgcn_readlane(ti, i);
+      dd.t[i] = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)(tiles + uni64((int64_t)(tix >= 0 ? tix : 0) * TBYTES)), 0,
+          tix >= 0 ? (int)TBYTES : 0, kBufferFlags);
+    }
+    const int64_t col0 = (int64_t)(grow0 + J) * B;      // first key column of the block
+#pragma unroll
+    for (int j = 0; j < VP; ++j) {
+      const bool on = valid && v_head[j] >= 0;
+      const int64_t off = uni64(on ? (int64_t)v_head[j] * vhead_elems + col0 * D : 0);
+      dd.v[j] = __builtin_amdgcn_make_buffer_rsrc((void *)(vt + off), 0, on ? B * D * 2 : 0,
+                                                  kBufferFlags);
+    }
+  };
+  // step s of a block: every piece of the wave, memory -> LDS stage
+  auto dma = [&](char *stage, const Desc &dd, int s) {
+#pragma unroll
+    for (int i = 0; i < SP; ++i)
+      lds_load16<0>(dd.t[i], stage + i * C::SRC_BYTES + p_lds, p_goff, s * 512);
+#pragma unroll
+    for (int j = 0; j < VP; ++j)
+      if (v_slot[j] < kPairT)
+        lds_load16<kPairVPolicy>(dd.v[j], stage + v_lds[j], v_goff[j], s * C::V_BYTES);
+  };
+
+  f32x16 acc[RB][NB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[rb][nb] = zero16();
+
+  // one step from an LDS stage: mix, round, multiply with V (the MFMAs of the
+  // first row block interleave with the mix of the second)
+  auto compute = [&](const char *stage) {
+    if (ta < 0) return;
+    u32x4 bv[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) bv[nb] = *reinterpret_cast<const u32x4 *>(stage + boff + nb * 1024);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      u32x4 v[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        // a missing source (b >= its count) has coefficient 0 and reads slot 0
+        v[b] = *reinterpret_cast<const u32x4 *>(stage + soff_b[b] + aoff[rb]);
+      float mx[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx[e] = 0.f;
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          mx[2 * e] = fmaf(cf[rb][b], __uint_as_float(v[b][e] << 16), mx[2 * e]);
+          mx[2 * e + 1] = fmaf(cf[rb][b], __uint_as_float(v[b][e] & 0xffff0000u), mx[2 * e + 1]);
+        }
+      u32x4 am;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) am[e] = pack_bf16x2(mx[2 * e], mx[2 * e + 1]);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[rb][nb] = mfma_bf16(as_bf16x8(am), as_bf16x8(bv[nb]), acc[rb][nb]);
+    }
+  };
+  // end of a step: this wave's loads into the next stage have landed (a full
+  // drain: direct-to-LDS loads complete with no finer count to wait on), then
+  // the work-group barrier
+  auto step_end = [] {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  if (nsteps > 0) {
+    char *st0 = smem, *st1 = smem + C::STAGE;
+    Desc dc;
+    make_desc(dc, 0);
+    dma(st0, dc, 0);
+    step_end();
+    for (int k = 0; k < nblk; ++k) {
+      // steps s, s + 1 of block k, each prefetching the next step into the
+      // other stage; the last step of a block prefetches the next block's first
+#pragma unroll
+      for (int s = 0; s < KS; s += 2) {
+        dma(st1, dc, s + 1);
+        compute(st0);
+        step_end();
+        if (s + 2 == KS) make_desc(dc, k + 1);
+        dma(st0, dc, (s + 2) % KS);
+        compute(st1);
+        step_end();
+      }
+    }
+  }
+
+  if (ta < 0) return;
+  float *ot = o + (int64_t)ta * T * D;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int row0 = 64 * part + 32 * rb;
+    const int q = row0 / B;
+    if (q == 1 && !has1) continue;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int ip = Iq[q] * B + (row0 % B) + acc_row(r, lane);
+      if (ip < L) {
+        float *dst = ot + (tok0 + ip) * D + r32;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) __builtin_nontemporal_store(acc[rb][nb][r], dst + 32 * nb);
+      }
+    }
+  }
+}
+
+// The apply kernels for one tile format, over `nrows` block-rows of `sched`.
+// bf16 maps: targets with at most four sources in pairs (k_pairs, then
+// k_apply_pair over the query-block pairs of `psched`); fp8 maps: one target
+// per work-group (k_apply4).  Targets with
+// more sources: k_apply_mix.  A work-group with nothing of its class returns
+// right after reading the weights.
 template <int B, int D, int FMT>
 static mf_status launch_apply_fmt(hipStream_t s, const mf_bsr_map *map, const float *W, int32_t Ht,
                                   int32_t Hkv, const SeqGeom &g, int32_t renorm, float *o,
                                   void *ws, const VtWs &w, const int32_t *sched, int32_t nrows,
-                                  int nbw, size_t smem, size_t smem_mix, size_t vbufs,
-                                  size_t vbufs_mix) {
+                                  const int32_t *psched, int32_t npairs, int nbw, size_t smem,
+                                  size_t smem_mix, size_t vbufs, size_t vbufs_mix) {
   using CM = ApplyMixCfg<B, D, FMT>;
-  if (smem + vbufs > 64 * 1024 &&
-      hipFuncSetAttribute(reinterpret_cast<const void *>(&k_apply4<B, D, FMT>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
-    return MF_ERR_HIP;
   if (smem_mix + vbufs_mix > 64 * 1024 &&
       hipFuncSetAttribute(reinterpret_cast<const void *>(&k_apply_mix<B, D, FMT>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem_mix) != hipSuccess)
     return MF_ERR_HIP;
   const char *tiles = static_cast<const char *>(map->tiles);
   const int64_t npos = ((int64_t)nrows + kXcds - 1) / kXcds * kXcds;
-  // one launch per source-count class; a work-group whose targets are all of
-  // the other class returns right after reading their weight rows
-  hipLaunchKernelGGL((k_apply4<B, D, FMT>), dim3((unsigned)(npos * Ht)),
-                     dim3(Apply4Cfg<B, D, FMT>::NT), smem, s, map->row_ptr, map->col_idx, tiles,
-                     map->kept_mass, map->num_heads, g.NBR, g.T, W, Ht, Ht / Hkv,
-                     at<uint16_t>(ws, w.vt), at<RowInfo>(ws, w.rt.rows), sched, nrows, nbw,
-                     map->capacity_tiles, renorm, o, map->row_alias);
+  if constexpr (FMT == MF_TILE_BF16) {
+    using CP = PairCfg<B, D>;
+    const size_t smem_pair = (size_t)pair_tables<B, D>(nbw).total;
+    if (smem_pair > 160 * 1024) return MF_ERR_UNSUPPORTED;
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&k_apply_pair<B, D>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem_pair) != hipSuccess)
+      return MF_ERR_HIP;
+    int32_t *gtab = at<int32_t>(ws, w.gtab);
+    hipLaunchKernelGGL(k_pairs, dim3(1), dim3(64), 0, s, W, Ht, map->num_heads, gtab);
+    if (hip_status() != MF_OK) return MF_ERR_HIP;
+    // any two targets with at most four sources fit one work-group
+    const int32_t ngmax = (Ht + 1) / 2;
+    const int64_t nppos = ((int64_t)npairs + kXcds - 1) / kXcds * kXcds;
+    if (npairs > 0)
+      hipLaunchKernelGGL((k_apply_pair<B, D>), dim3((unsigned)(nppos * ngmax)), dim3(CP::NT),
+                         smem_pair, s, map->row_ptr, map->col_idx, tiles, map->kept_mass,
+                         map->num_heads, g.NBR, g.T, W, Ht / Hkv, at<uint16_t>(ws, w.vt),
+                         at<RowInfo>(ws, w.rt.rows), psched, npairs, nbw, map->capacity_tiles,
+                         renorm, o, map->row_alias, gtab, ngmax);
+  } else {
+    if (smem + vbufs > 64 * 1024 &&
+        hipFuncSetAttribute(reinterpret_cast<const void *>(&k_apply4<B, D, FMT>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
+      return MF_ERR_HIP;
+    hipLaunchKernelGGL((k_apply4<B, D, FMT>), dim3((unsigned)(npos * Ht)),
+                       dim3(Apply4Cfg<B, D, FMT>::NT), smem, s, map->row_ptr, map->col_idx, tiles,
+                       map->kept_mass, map->num_heads, g.NBR, g.T, W, Ht, Ht / Hkv,
+                       at<uint16_t>(ws, w.vt), at<RowInfo>(ws, w.rt.rows), sched, nrows, nbw,
+                       map->capacity_tiles, renorm, o, map->row_alias);
+  }
   if (hip_status() != MF_OK) return MF_ERR_HIP;
   const int64_t ngrp = (Ht + CM::G - 1) / CM::G;
   hipLaunchKernelGGL((k_apply_mix<B, D, FMT>), dim3((unsigned)(npos * ngrp)), dim3(CM::NT),
@@ -1067,8 +1677,8 @@ static mf_status launch_apply_fmt(hipStream_t s, const mf_bsr_map *map, const fl
 // V staging, the window schedule (if any), then both apply kernels.
 template <int B, int D>
 static mf_status launch_apply(hipStream_t s, const mf_bsr_map *map, const float *W, int32_t Ht,
-                              const VSrc &vs, const SeqGeom &g, int32_t nrows, int32_t renorm,
-                              float *o, void *ws, const VtWs &w) {
+                              const VSrc &vs, const SeqGeom &g, int32_t nrows, int32_t npairs,
+                              int32_t renorm, float *o, void *ws, const VtWs &w) {
   const int nbw = (g.maxnb + 31) / 32 > 0 ? (g.maxnb + 31) / 32 : 1;
   const size_t smem = apply_smem(B, map->num_heads, nbw);
   const size_t smem_mix = mix_smem(B, map->num_heads, nbw);
@@ -1076,16 +1686,20 @@ static mf_status launch_apply(hipStream_t s, const mf_bsr_map *map, const float 
   // offsets d * NBR * B * 2
   if (map->capacity_tiles > INT32_MAX) return MF_ERR_UNSUPPORTED;
   if ((int64_t)D * g.NBR * B * 2 >= ((int64_t)1 << 31)) return MF_ERR_UNSUPPORTED;
-  if (map->num_heads > kMixMaxSources) return MF_ERR_UNSUPPORTED;
+  if (map->num_heads > kMixMaxSources || Ht > kMaxTargets) return MF_ERR_UNSUPPORTED;
   const size_t vbufs = 2 * (size_t)B * D * 2;  // the two static V tile buffers of k_apply4
   const size_t vbufs_mix = (size_t)ApplyMixCfg<B, D, MF_TILE_BF16>::G * B * D * 2;
   if (smem + vbufs > 160 * 1024 || smem_mix + vbufs_mix > 160 * 1024) return MF_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL((k_vtranspose<B, D>), dim3(g.NBR, vs.Hkv), dim3(256), 0, s, vs, g.T,
+  hipLaunchKernelGGL((k_vstage<B, D>), dim3(g.NBR, vs.Hkv), dim3(256), 0, s, vs, g.T,
                      at<RowInfo>(ws, w.rt.rows), g.NBR, at<uint16_t>(ws, w.vt));
   if (hip_status() != MF_OK) return MF_ERR_HIP;
   const int32_t *sched = at<int32_t>(ws, w.rt.sched);
+  if (nrows == 0) return MF_OK;
+  int32_t *psched = at<int32_t>(ws, w.psched);
+  hipLaunchKernelGGL(k_pair_sched, dim3(1), dim3(1024), 0, s, at<RowInfo>(ws, w.rt.rows), sched,
+                     g.NBR, B, vs.window, psched);
+  if (hip_status() != MF_OK) return MF_ERR_HIP;
   if (vs.window) {
-    if (nrows == 0) return MF_OK;
     hipLaunchKernelGGL(k_window_sched, dim3(1), dim3(1024), 0, s, at<RowInfo>(ws, w.rt.rows),
                        sched, g.NBR, B, vs.window, at<int32_t>(ws, w.wsched));
     if (hip_status() != MF_OK) return MF_ERR_HIP;
@@ -1093,9 +1707,11 @@ static mf_status launch_apply(hipStream_t s, const mf_bsr_map *map, const float 
   }
   if (map->tile_format == MF_TILE_MXFP8)
     return launch_apply_fmt<B, D, MF_TILE_MXFP8>(s, map, W, Ht, vs.Hkv, g, renorm, o, ws, w, sched,
-                                                 nrows, nbw, smem, smem_mix, vbufs, vbufs_mix);
+                                                 nrows, psched, npairs, nbw, smem, smem_mix, vbufs,
+                                                 vbufs_mix);
   return launch_apply_fmt<B, D, MF_TILE_BF16>(s, map, W, Ht, vs.Hkv, g, renorm, o, ws, w, sched,
-                                              nrows, nbw, smem, smem_mix, vbufs, vbufs_mix);
+                                              nrows, psched, npairs, nbw, smem, smem_mix, vbufs,
+                                              vbufs_mix);
 }
 
 // Shared argument checks and dispatch of both apply entry points.
@@ -1118,7 +1734,8 @@ static mf_status apply_common(void *stream, const mf_bsr_map *map, const float *
                   !map->kept_mass))
     return MF_ERR_INVALID_ARG;
   const int B = map->block;
-  int64_t nrows = g.NBR;
+  int64_t nrows = g.NBR, npairs = 0;  // block-rows, and query-block pairs of the fused retrieval
+  for (int32_t q = 0; q < nseq; ++q) npairs += ((cu_host[q + 1] - cu_host[q] + B - 1) / B + 1) / 2;
   if (vs.pages) {
     if (vs.page_size <= 0 || vs.num_pages <= 0 || vs.max_pages <= 0 || !vs.table)
       return MF_ERR_INVALID_ARG;
@@ -1129,6 +1746,7 @@ static mf_status apply_common(void *stream, const mf_bsr_map *map, const float *
   if (vs.window) {
     if (!window_host) return MF_ERR_INVALID_ARG;
     nrows = 0;
+    npairs = 0;
     for (int32_t s = 0; s < nseq; ++s) {
       const int32_t L = cu_host[s + 1] - cu_host[s];
       const int32_t a = window_host[2 * s], b = window_host[2 * s + 1];
@@ -1136,6 +1754,7 @@ static mf_status apply_common(void *stream, const mf_bsr_map *map, const float *
       if (a == b) continue;  // nothing of this sequence in the chunk
       if (a % B != 0 || (b % B != 0 && b != L)) return MF_ERR_INVALID_ARG;
       nrows += ((int64_t)b + B - 1) / B - a / B;
+      npairs += (((int64_t)b + B - 1) / B - a / B + 1) / 2;
     }
   }
   const VtWs w = vt_ws(g, Hkv, B, d);
@@ -1144,15 +1763,15 @@ static mf_status apply_common(void *stream, const mf_bsr_map *map, const float *
   void *wsa = reinterpret_cast<void *>((reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if ((st = launch_rowtable(s, cu_dev, g, B, wsa, w.rt)) != MF_OK) return st;
-  const int32_t nr = (int32_t)nrows;
+  const int32_t nr = (int32_t)nrows, np = (int32_t)npairs;
   if (B == 32)
-    return d == 64 ? launch_apply<32, 64>(s, map, W, Ht, vs, g, nr, renorm, o, wsa, w)
-                   : launch_apply<32, 128>(s, map, W, Ht, vs, g, nr, renorm, o, wsa, w);
+    return d == 64 ? launch_apply<32, 64>(s, map, W, Ht, vs, g, nr, np, renorm, o, wsa, w)
+                   : launch_apply<32, 128>(s, map, W, Ht, vs, g, nr, np, renorm, o, wsa, w);
   if (B == 64)
-    return d == 64 ? launch_apply<64, 64>(s, map, W, Ht, vs, g, nr, renorm, o, wsa, w)
-                   : launch_apply<64, 128>(s, map, W, Ht, vs, g, nr, renorm, o, wsa, w);
-  return d == 64 ? launch_apply<128, 64>(s, map, W, Ht, vs, g, nr, renorm, o, wsa, w)
-                 : launch_apply<128, 128>(s, map, W, Ht, vs, g, nr, renorm, o, wsa, w);
+    return d == 64 ? launch_apply<64, 64>(s, map, W, Ht, vs, g, nr, np, renorm, o, wsa, w)
+                   : launch_apply<64, 128>(s, map, W, Ht, vs, g, nr, np, renorm, o, wsa, w);
+  return d == 64 ? launch_apply<128, 64>(s, map, W, Ht, vs, g, nr, np, renorm, o, wsa, w)
+                 : launch_apply<128, 128>(s, map, W, Ht, vs, g, nr, np, renorm, o, wsa, w);
 }
 
 }  // namespace mf

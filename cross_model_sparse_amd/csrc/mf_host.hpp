@@ -123,9 +123,13 @@ inline CompressWs compress_ws(const SeqGeom &g, int32_t Hs, int32_t B) {
 // schedule of a query window.
 struct VtWs {
   RowTable rt;
-  size_t vt, wsched;
+  size_t vt, wsched, gtab, psched;
   size_t total;
 };
+
+// Target-group table of the apply path: a count, then up to 1024 groups of at
+// most 4 targets.
+constexpr int kGroupTableInts = 1 + 4 * 1024;
 
 inline VtWs vt_ws(const SeqGeom &g, int32_t Hkv, int32_t B, int32_t d) {
   Carve c;
@@ -133,6 +137,8 @@ inline VtWs vt_ws(const SeqGeom &g, int32_t Hkv, int32_t B, int32_t d) {
   w.rt = carve_rows(c, g);
   w.vt = c.take<uint16_t>((size_t)Hkv * d * (size_t)(g.NBR > 0 ? g.NBR : 1) * B);
   w.wsched = c.take<int32_t>(g.NBR > 0 ? g.NBR : 1);
+  w.gtab = c.take<int32_t>(kGroupTableInts);
+  w.psched = c.take<int32_t>(2 * (size_t)(g.NBR > 0 ? g.NBR : 1));
   w.total = c.off + 256;
   return w;
 }
