@@ -21,6 +21,7 @@
 // and reuse its L2 copy of the source tiles, while the 8 XCDs work on 8 query
 // blocks at once and share V through the memory-side cache.
 #include "mf_host.hpp"
+#include <mutex>
 
 namespace mf {
 
@@ -1714,11 +1715,41 @@ static mf_status launch_apply(hipStream_t s, const mf_bsr_map *map, const float 
                                               vbufs_mix);
 }
 
-// Shared argument checks and dispatch of both apply entry points.
+}  // namespace mf
+
+// Fixed device scratch of mf_apply_translated_noalloc.  Each GPU the library
+// runs on holds its own copy until the process ends.  Host code never passes
+// `scratch` itself (its host-side name is not a device address): it uses the
+// per-device address that hipGetSymbolAddress returns.
+static __device__ __align__(256) unsigned char scratch[MF_APPLY_NOALLOC_SCRATCH_BYTES];
+
+namespace mf {
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void *g_scratch_dev[kMaxDevices];
+
+// Device address of the current device's scratch, looked up once per device
+// (with that device current); nullptr if the lookup fails.
+static void *scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_dev[dev] = ptr;
+  }
+  return g_scratch_dev[dev];
+}
+
+
+// Shared argument checks and dispatch of the apply entry points.  With
+// use_scratch the workspace is the fixed device scratch instead of ws.
 static mf_status apply_common(void *stream, const mf_bsr_map *map, const float *W, int32_t Ht,
                               VSrc vs, int32_t d, const int32_t *cu_host, const int32_t *cu_dev,
                               int32_t nseq, const int32_t *window_host, int32_t renorm, float *o,
-                              void *ws, size_t ws_bytes) {
+                              void *ws, size_t ws_bytes, bool use_scratch = false) {
   const int32_t Hkv = vs.Hkv;
   if (!map || !cu_host || !cu_dev || Ht <= 0 || Hkv <= 0 || Ht % Hkv != 0)
     return MF_ERR_INVALID_ARG;
@@ -1758,6 +1789,13 @@ static mf_status apply_common(void *stream, const mf_bsr_map *map, const float *
     }
   }
   const VtWs w = vt_ws(g, Hkv, B, d);
+  if (use_scratch) {
+    if (w.total > MF_APPLY_NOALLOC_SCRATCH_BYTES) return MF_ERR_WORKSPACE;
+    if (g.NBR == 0) return MF_OK;
+    ws = scratch_address();
+    ws_bytes = MF_APPLY_NOALLOC_SCRATCH_BYTES;
+    if (!ws) return MF_ERR_HIP;
+  }
   if (!ws || ws_bytes < w.total) return MF_ERR_WORKSPACE;
   if (g.NBR == 0) return MF_OK;
   void *wsa = reinterpret_cast<void *>((reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255));
@@ -1793,6 +1831,16 @@ extern "C" mf_status mf_apply_translated(void *stream, const mf_bsr_map *map, co
   VSrc vs{static_cast<const uint16_t *>(v), nullptr, nullptr, 0, 0, 0, Hkv, nullptr};
   return apply_common(stream, map, W, Ht, vs, d, cu_host, cu_dev, nseq, nullptr, renorm, o, ws,
                       ws_bytes);
+}
+
+extern "C" mf_status mf_apply_translated_noalloc(void *stream, const mf_bsr_map *map,
+                                                 const float *W, int32_t Ht, const void *v,
+                                                 int32_t Hkv, int32_t d,
+                                                 const int32_t *cu_host, const int32_t *cu_dev,
+                                                 int32_t nseq, int32_t renorm, float *o) {
+  VSrc vs{static_cast<const uint16_t *>(v), nullptr, nullptr, 0, 0, 0, Hkv, nullptr};
+  return apply_common(stream, map, W, Ht, vs, d, cu_host, cu_dev, nseq, nullptr, renorm, o,
+                      nullptr, 0, true);
 }
 
 extern "C" mf_status mf_apply_translated_paged(void *stream, const mf_bsr_map *map,

@@ -27,7 +27,11 @@ EXPORTS = ("mf_num_block_rows", "mf_compress_max_tiles", "mf_compress_workspace_
            "mf_dense_workspace_bytes", "mf_dense_ref_attention", "mf_read_status",
            "mf_status_string", "mf_prefix_dedupe_workspace_bytes", "mf_prefix_dedupe",
            "mf_tile_bytes", "mf_tv_distance_workspace_bytes", "mf_tv_distance",
-           "mf_apply_translated_paged")
+           "mf_apply_translated_paged", "mf_apply_translated_noalloc")
+
+# Bytes of the fixed per-GPU scratch of mf_apply_translated_noalloc
+# (MF_APPLY_NOALLOC_SCRATCH_BYTES in include/mapflow.h).
+APPLY_NOALLOC_SCRATCH_BYTES = 128 << 20
 
 
 class MfLogitBias(ctypes.Structure):
@@ -86,6 +90,8 @@ def load():
         "mf_prefix_dedupe_workspace_bytes": (sz, [pcu, i32, i32]),
         "mf_prefix_dedupe": (i32, [vp, vp, vp, i32, pcu, vp, i32, i32, i32, i32, vp, vp, sz]),
         "mf_tile_bytes": (i64, [i32, i32]),
+        "mf_apply_translated_noalloc": (i32, [vp, ctypes.POINTER(MfBsrMap), vp, i32, vp, i32, i32, pcu,
+                                              vp, i32, i32, vp]),
         "mf_apply_translated_paged": (i32, [vp, ctypes.POINTER(MfBsrMap), vp, i32, ctypes.POINTER(MfPagedV),
                                             i32, i32, pcu, vp, i32, pcu, vp, i32, vp, vp, sz]),
         "mf_tv_distance_workspace_bytes": (sz, [pcu, i32, i32]),
@@ -350,6 +356,36 @@ def mf_apply_translated(m: BsrMap, W: torch.Tensor, v: torch.Tensor, cu_seqlens,
                                  _cu_ptr(cu), cu_dev.data_ptr(), len(cu) - 1, int(bool(renorm)),
                                  out.data_ptr(), workspace.data_ptr(), workspace.numel())
     _check("mf_apply_translated", st)
+    return out
+
+
+def mf_apply_translated_noalloc(m: BsrMap, W: torch.Tensor, v: torch.Tensor, cu_seqlens,
+                                renorm: bool = True, out: Optional[torch.Tensor] = None,
+                                cu_dev: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """mf_apply_translated with the library's fixed per-GPU scratch in place of a
+    workspace: the native call allocates nothing.  Pass `out` and `cu_dev` to
+    keep the binding from allocating them.  Calls that overlap on one GPU race."""
+    lib = load()
+    cu = _cu_host(cu_seqlens)
+    Ht = W.shape[0]
+    Hkv, T, d = v.shape
+    if v.dtype != torch.bfloat16 or not v.is_contiguous():
+        raise ValueError("v must be contiguous bfloat16")
+    if W.dtype != torch.float32 or not W.is_contiguous() or W.dim() != 2 or W.shape[1] != m.num_heads:
+        raise ValueError("W must be contiguous float32 [Ht, Hs]")
+    _check_tokens("v", v, cu)
+    dev = v.device
+    if out is None:
+        out = torch.empty((Ht, T, d), dtype=torch.float32, device=dev)
+    else:
+        _check_out(out, (Ht, T, d))
+    if cu_dev is None:
+        cu_dev = _dev_cu(cu, dev)
+    cs = m.cstruct()
+    st = lib.mf_apply_translated_noalloc(_stream(), ctypes.byref(cs), W.data_ptr(), Ht, v.data_ptr(), Hkv,
+                                         d, _cu_ptr(cu), cu_dev.data_ptr(), len(cu) - 1,
+                                         int(bool(renorm)), out.data_ptr())
+    _check("mf_apply_translated_noalloc", st)
     return out
 
 

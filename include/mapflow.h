@@ -234,8 +234,8 @@ mf_status mf_prefix_dedupe(void *stream, const void *q, const void *k, mf_dtype 
                            void *workspace, size_t workspace_bytes);
 
 /* Device workspace bytes mf_apply_translated and mf_apply_translated_paged need:
- * a block-padded, transposed copy of V ([Hkv][d][NBR * B] bf16), the block-row
- * table and a window schedule.  0 if invalid. */
+ * a block-padded copy of V staged in 16-key chunks ([Hkv][NBR * B / 16][d][16]
+ * bf16), the block-row table and the query-block schedules.  0 if invalid. */
 size_t mf_apply_workspace_bytes(int32_t Hkv, const int32_t *cu_seqlens_host, int32_t nseq,
                                 int32_t B, int32_t d);
 
@@ -261,6 +261,31 @@ mf_status mf_apply_translated(void *stream, const mf_bsr_map *map, const float *
                               const int32_t *cu_seqlens_host, const int32_t *cu_seqlens_dev,
                               int32_t nseq, int32_t renorm, float *o, void *workspace,
                               size_t workspace_bytes);
+
+/* Bytes of the fixed device scratch that mf_apply_translated_noalloc uses in
+ * place of a workspace (per GPU, held until the process ends). */
+#define MF_APPLY_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+/* mf_apply_translated without a workspace argument and without any device
+ * allocation, for callers that cannot allocate: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same computation,
+ * kernels and output as mf_apply_translated.
+ *
+ * The workspace lives in a static device array of
+ * MF_APPLY_NOALLOC_SCRATCH_BYTES bytes; a call whose
+ * mf_apply_workspace_bytes(Hkv, cu_seqlens, nseq, map->block, d) exceeds it
+ * returns MF_ERR_WORKSPACE (Hkv = 8, d = 128, B = 128 fits up to 65408 tokens).
+ * Nothing in the scratch has to start at zero, and each call rewrites what it
+ * reads.  The array is looked up on the first call on each device (the device
+ * current at the call, which must be the stream's).  All calls on one GPU
+ * share that array: calls that overlap in time on one GPU (different streams,
+ * or host threads without ordering) race on it and give undefined output.
+ * Errors: MF_ERR_INVALID_ARG, MF_ERR_UNSUPPORTED, MF_ERR_WORKSPACE, MF_ERR_HIP. */
+mf_status mf_apply_translated_noalloc(void *stream, const mf_bsr_map *map, const float *W,
+                                      int32_t Ht, const void *v, int32_t Hkv, int32_t d,
+                                      const int32_t *cu_seqlens_host,
+                                      const int32_t *cu_seqlens_dev, int32_t nseq,
+                                      int32_t renorm, float *o);
 
 /* V held in a paged cache (PagedAttention-style): token j of sequence s is at
  * slot j % page_size of page block_table[s * max_pages_per_seq + j / page_size]

@@ -30,7 +30,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = header_functions()
-    assert len(names) == 16
+    assert len(names) == 17
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(mf.EXPORTS) == names
@@ -211,3 +211,25 @@ def test_status_strings(lib):
     for s in range(6):
         assert lib.mf_status_string(s).decode() not in ("", "unknown status")
     assert lib.mf_status_string(99).decode() == "unknown status"
+
+
+def test_apply_noalloc_rejects_before_touching_the_device(lib):
+    """Invalid arguments and inputs whose workspace would exceed the fixed scratch
+    are refused on the host (no device call is made on these paths)."""
+    fake = ctypes.c_void_p(16)
+    f = lib.mf_apply_translated_noalloc
+    c = cu([100])
+    pc = c.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    m = mf.MfBsrMap(2, 32, 4, 100, 10, 8, 8, 8, 8, 8, 8, None, 0)
+    assert f(None, ctypes.byref(m), fake, 4, fake, 3, 64, pc, fake, 1, 1, fake) == mf.MF_ERR_INVALID_ARG
+    assert f(None, ctypes.byref(m), fake, 4, fake, 2, 80, pc, fake, 1, 1, fake) == mf.MF_ERR_UNSUPPORTED
+    assert f(None, None, fake, 4, fake, 2, 64, pc, fake, 1, 1, fake) == mf.MF_ERR_INVALID_ARG
+    # the workspace of Hkv = 8, d = 128, B = 128 outgrows the scratch past 65408 tokens
+    lim = mf.APPLY_NOALLOC_SCRATCH_BYTES
+    for L, fits in ((65408, True), (65409, False), (32768 * 4, False)):
+        c = cu([L])
+        pc = c.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+        assert (0 < mf.mf_apply_workspace_bytes(8, c, 128, 128) <= lim) == fits
+        if not fits:
+            m = mf.MfBsrMap(8, 128, (L + 127) // 128, L, 10, 8, 8, 8, 8, 8, 8, None, 0)
+            assert f(None, ctypes.byref(m), fake, 8, fake, 8, 128, pc, fake, 1, 1, fake) == mf.MF_ERR_WORKSPACE
