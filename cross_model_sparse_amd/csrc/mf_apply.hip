@@ -1061,16 +1061,16 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(2))) void
 // number on ties).  Any two such targets fit (at most 8 sources).  Targets with
 // more than four sources are left to k_apply_mix.
 //
-// gtab[0] = number of pairs; pair q holds targets gtab[1 + 2q], gtab[2 + 2q]
-// (-1 for an empty slot).  One wave; Ht <= kMaxTargets, Hs <= kMixMaxSources.
+// gtab[0] = number of groups; group q holds targets gtab[1 + 2q], gtab[2 + 2q]
+// (-1 for an empty slot).  With pair == 0 every such target forms a group of
+// its own.  One wave; Ht <= kMaxTargets, Hs <= kMixMaxSources.
 // ---------------------------------------------------------------------------
-constexpr int kPairT = 2;          // targets per work-group
-constexpr int kPairU = 8;          // sources of a work-group (their union)
+constexpr int kPairT = 2;          // targets per work-group of the translated retrieval
 constexpr int kMaxTargets = 1024;
 constexpr int kMixMaxSources = 128;
 
 __global__ __launch_bounds__(64) void k_pairs(const float *__restrict__ W, int32_t Ht, int32_t Hs,
-                                              int32_t *__restrict__ gtab) {
+                                              int32_t pair, int32_t *__restrict__ gtab) {
   __shared__ uint32_t msk[kMaxTargets][4];
   __shared__ uint8_t state[kMaxTargets];  // 0 free, 1 placed, 2 not handled here
   const int lane = threadIdx.x;
@@ -1100,7 +1100,7 @@ __global__ __launch_bounds__(64) void k_pairs(const float *__restrict__ W, int32
     if (lane == 0) state[first] = 1;
     __syncthreads();
     int best = INT32_MAX;
-    for (int t = lane; t < Ht; t += 64) {
+    for (int t = lane; pair && t < Ht; t += 64) {
       if (state[t] != 0) continue;
       int nu = 0;
 #pragma unroll
@@ -1193,12 +1193,12 @@ __global__ __launch_bounds__(1024) void k_pair_sched(const RowInfo *__restrict__
 // MFMAs into fp32 accumulators; each V operand read serves two 32-row blocks.
 // The translated map never leaves registers.
 //
-// Loads: per key block, each wave builds one buffer descriptor per source
-// piece (a tile of one query block, zero-length where the source kept no tile)
-// and per V piece; steps inside the block only move the scalar offset.  The
-// loads of step q + 2 go to a register stage while step q is computed from one
-// LDS stage and step q + 1 moves to the other; one barrier per step.  Every
-// lane issues the same number of loads every step, so wait counts are exact.
+// Loads go straight from memory to LDS (buffer loads with an LDS target), two
+// stages: step q + 1 moves into one while step q is computed from the other;
+// one barrier per step.  A wave loads, for U / (waves per query block) of the
+// source slots, all rows of one query block, so per key block it builds only
+// that many tile descriptors (zero-length where a source kept no tile) plus
+// one per V piece; steps inside the block move the scalar offset only.
 //
 // Order: consecutive work-group ids go to the XCDs in turn.  One XCD runs all
 // target pairs of one query-block pair at a time (32 work-groups for 64
@@ -1210,24 +1210,27 @@ __global__ __launch_bounds__(1024) void k_pair_sched(const RowInfo *__restrict__
 // ---------------------------------------------------------------------------
 constexpr int kPairVPolicy = 0;    // cache policy of the V loads
 
-template <int B, int D>
+template <int B, int D, int TP>
 struct PairCfg {
+  static constexpr int U = 4 * TP;                      // source slots (their union)
   static constexpr int ROWS = 2 * B;                    // rows of a work-group
   static constexpr int WPT = ROWS >= 128 ? ROWS / 64 : 1;   // waves per target
-  static constexpr int NW = kPairT * WPT;
+  static constexpr int NW = TP * WPT;
   static constexpr int NT = NW * 64;
   static constexpr int RB = ROWS / (32 * WPT);          // 32-row blocks per wave
   static constexpr int NB = D / 32;                     // 32-column blocks
   static constexpr int KS = B / 16;                     // 16-key steps per key block
   static constexpr int SRC_BYTES = ROWS * 32;           // a source's slice of one step
   static constexpr int V_BYTES = D * 32;                // a target's V slice of one step
-  static constexpr int V_OFF = kPairU * SRC_BYTES;
-  static constexpr int STAGE = V_OFF + kPairT * V_BYTES;
-  static constexpr int SP = kPairU * SRC_BYTES / 16 / NT;               // source pieces per lane
-  static constexpr int VPIECES = kPairT * V_BYTES / 16;
+  static constexpr int V_OFF = U * SRC_BYTES;
+  static constexpr int STAGE = V_OFF + TP * V_BYTES;
+  static constexpr int WQ = NW / 2;                     // waves per query block
+  static constexpr int NBQ = B / 32;                    // 1 KB blocks of a query block's slice
+  static constexpr int SPW = U / WQ;                    // slots whose pieces a wave loads
+  static constexpr int SP = SPW * NBQ;                  // source pieces per lane
+  static constexpr int VPIECES = TP * V_BYTES / 16;
   static constexpr int VP = (VPIECES + NT - 1) / NT;                    // V pieces per lane
-  static constexpr int NP = SP + VP;
-  static_assert(2 * ROWS == NT, "a lane's source pieces are one per slot");
+  static_assert(NW % 2 == 0 && U % WQ == 0 && SP == 8, "every wave loads 8 source blocks per step");
   static_assert(RB == 2 && (2 * D) % 64 == 0 && KS % 2 == 0, "layout assumptions");
 };
 
@@ -1235,22 +1238,22 @@ struct PairCfg {
 struct PairTables {
   int rbase, rend, usrc, smap, sw, sns, stgt, umask, misc, bm, pc, uni, upre, blist, total;
 };
-template <int B, int D>
+template <int B, int D, int TP>
 __host__ __device__ inline PairTables pair_tables(int nbw) {
-  using C = PairCfg<B, D>;
+  using C = PairCfg<B, D, TP>;
   PairTables t;
   int o = 2 * C::STAGE;
-  t.rbase = o; o += 2 * kPairU * 8;
-  t.rend = o; o += 2 * kPairU * 8;
-  t.usrc = o; o += kPairU * 4;
+  t.rbase = o; o += 2 * C::U * 8;
+  t.rend = o; o += 2 * C::U * 8;
+  t.usrc = o; o += C::U * 4;
   t.smap = o; o += 8 * 4;
   t.sw = o; o += 8 * 4;
   t.sns = o; o += 4 * 4;
   t.stgt = o; o += 4 * 4;
   t.umask = o; o += 4 * 4;
   t.misc = o; o += 4 * 4;
-  t.bm = o; o += 2 * kPairU * nbw * 4;
-  t.pc = o; o += 2 * kPairU * nbw * 4;
+  t.bm = o; o += 2 * C::U * nbw * 4;
+  t.pc = o; o += 2 * C::U * nbw * 4;
   t.uni = o; o += nbw * 4;
   t.upre = o; o += nbw * 4;
   t.blist = o; o += nbw * 32 * 4;
@@ -1258,8 +1261,8 @@ __host__ __device__ inline PairTables pair_tables(int nbw) {
   return t;
 }
 
-template <int B, int D>
-__global__ __launch_bounds__((PairCfg<B, D>::NT)) __attribute__((amdgpu_waves_per_eu(2)))
+template <int B, int D, int TP>
+__global__ __launch_bounds__((PairCfg<B, D, TP>::NT)) __attribute__((amdgpu_waves_per_eu(2)))
 void k_apply_pair(const int64_t *__restrict__ row_ptr, const int32_t *__restrict__ col_idx,
                   const char *__restrict__ tiles, const float *__restrict__ kept_mass, int32_t Hs,
                   int32_t NBR, int64_t T, const float *__restrict__ W, int32_t grp,
@@ -1268,18 +1271,19 @@ void k_apply_pair(const int64_t *__restrict__ row_ptr, const int32_t *__restrict
                   int64_t capacity, int32_t renorm, float *__restrict__ o,
                   const int32_t *__restrict__ row_alias, const int32_t *__restrict__ gtab,
                   int32_t ngmax) {
-  using C = PairCfg<B, D>;
-  constexpr int RB = C::RB, NB = C::NB, KS = C::KS, SP = C::SP, VP = C::VP, NP = C::NP;
+  using C = PairCfg<B, D, TP>;
+  constexpr int RB = C::RB, NB = C::NB, KS = C::KS, VP = C::VP, U_MAX = C::U;
+  constexpr int SPW = C::SPW, NBQ = C::NBQ;
   constexpr int64_t TBYTES = (int64_t)B * B * 2;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const PairTables tb = pair_tables<B, D>(nbw);
+  const PairTables tb = pair_tables<B, D, TP>(nbw);
   int64_t *rbase = reinterpret_cast<int64_t *>(smem + tb.rbase);  // [2][U] first tile of the row
   int64_t *rend = reinterpret_cast<int64_t *>(smem + tb.rend);    // [2][U] end (capped)
   int32_t *usrc = reinterpret_cast<int32_t *>(smem + tb.usrc);    // [U] source head
-  int32_t *smap = reinterpret_cast<int32_t *>(smem + tb.smap);    // [2][4] slot of source b of target a
-  float *sw = reinterpret_cast<float *>(smem + tb.sw);            // [2][4] weight
-  int32_t *sns = reinterpret_cast<int32_t *>(smem + tb.sns);      // [2] source count
-  int32_t *stgt = reinterpret_cast<int32_t *>(smem + tb.stgt);    // [2] target or -1
+  int32_t *smap = reinterpret_cast<int32_t *>(smem + tb.smap);    // [TP][4] slot of source b of target a
+  float *sw = reinterpret_cast<float *>(smem + tb.sw);            // [TP][4] weight
+  int32_t *sns = reinterpret_cast<int32_t *>(smem + tb.sns);      // [TP] source count
+  int32_t *stgt = reinterpret_cast<int32_t *>(smem + tb.stgt);    // [TP] target or -1
   uint32_t *umask = reinterpret_cast<uint32_t *>(smem + tb.umask);
   int32_t *misc = reinterpret_cast<int32_t *>(smem + tb.misc);    // [0] union blocks
   uint32_t *bm = reinterpret_cast<uint32_t *>(smem + tb.bm);      // [2][U][nbw] kept bitmaps
@@ -1289,7 +1293,7 @@ void k_apply_pair(const int64_t *__restrict__ row_ptr, const int32_t *__restrict
   int32_t *blist = reinterpret_cast<int32_t *>(smem + tb.blist);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // work-group -> (query-block pair, target pair)
+  // work-group -> (query-block pair, target group)
   const int x = blockIdx.x % kXcds, kx = blockIdx.x / kXcds;
   const int round = kx / ngmax, gi = kx % ngmax;
   const int pidx = round * kXcds + ((round & 1) ? (kXcds - 1 - x) : x);
@@ -1316,10 +1320,10 @@ void k_apply_pair(const int64_t *__restrict__ row_ptr, const int32_t *__restrict
 
   // ---- set-up: targets, their sources, the source union -------------------
   if (tid < 4) umask[tid] = 0u;
-  if (tid < kPairT) stgt[tid] = gtab[1 + 2 * gi + tid];
-  for (int i = tid; i < 2 * kPairU * nbw; i += C::NT) bm[i] = 0u;
+  if (tid < TP) stgt[tid] = gtab[1 + 2 * gi + tid];
+  for (int i = tid; i < 2 * U_MAX * nbw; i += C::NT) bm[i] = 0u;
   __syncthreads();
-  if (wave < kPairT) {
+  if (wave < TP) {
     const int t = stgt[wave];
     int ns = 0;
     if (t >= 0)
@@ -1350,47 +1354,47 @@ void k_apply_pair(const int64_t *__restrict__ row_ptr, const int32_t *__restrict
     if (w > 2) r += __popc(um2);
     return r;
   };
-  const int U = __popc(um0) + __popc(um1) + __popc(um2) + __popc(um3);  // <= kPairU
-  if (tid < kMixMaxSources) {
-    const int h = tid;
+  const int U = __popc(um0) + __popc(um1) + __popc(um2) + __popc(um3);  // <= U_MAX
+  for (int h = tid; h < kMixMaxSources; h += C::NT) {
     if ((umask[h >> 5] >> (h & 31)) & 1u) {
       const int u = slot_of(h);
       usrc[u] = h;
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         const bool on = b == 0 || has1;
-        rbase[b * kPairU + u] = on ? row_ptr[(int64_t)h * NBR + grmq[b]] : 0;
-        rend[b * kPairU + u] = on ? min(row_ptr[(int64_t)h * NBR + grmq[b] + 1], capacity) : 0;
+        rbase[b * U_MAX + u] = on ? row_ptr[(int64_t)h * NBR + grmq[b]] : 0;
+        rend[b * U_MAX + u] = on ? min(row_ptr[(int64_t)h * NBR + grmq[b] + 1], capacity) : 0;
       }
     }
   }
   __syncthreads();
-  if (tid < 8) {
+  if (tid < 4 * TP) {
     const int a = tid >> 2, b = tid & 3;
     smap[tid] = b < sns[a] ? slot_of(smap[tid]) : 0;
   }
   // kept bitmaps of the union's sources, both query blocks
   for (int bu = 0; bu < 2 * U; ++bu) {
     const int b = bu / U, u = bu % U;
-    const int64_t e = rend[b * kPairU + u];
-    for (int64_t idx = rbase[b * kPairU + u] + tid; idx < e; idx += C::NT) {
+    const int64_t e = rend[b * U_MAX + u];
+    for (int64_t idx = rbase[b * U_MAX + u] + tid; idx < e; idx += C::NT) {
       const int J = col_idx[idx];
-      atomicOr(&bm[(b * kPairU + u) * nbw + (J >> 5)], 1u << (J & 31));
+      atomicOr(&bm[(b * U_MAX + u) * nbw + (J >> 5)], 1u << (J & 31));
     }
   }
   __syncthreads();
   const int nw_row = (n + 31) / 32;
-  for (int i = tid; i < 2 * kPairU * nw_row; i += C::NT) {
+  for (int i = tid; i < 2 * U_MAX * nw_row; i += C::NT) {
     // popcount prefix of each bitmap (its tile rank before word w)
     const int bu = i / nw_row, w = i % nw_row;
     int run = 0;
     for (int v = 0; v < w; ++v) run += __popc(bm[bu * nbw + v]);
     pc[bu * nbw + w] = run;
   }
-  if (tid < nw_row) {
+
+  for (int w = tid; w < nw_row; w += C::NT) {
     uint32_t v = 0u;
-    for (int bu = 0; bu < 2 * kPairU; ++bu) v |= bm[bu * nbw + tid];
-    uni[tid] = v;
+    for (int bu = 0; bu < 2 * U_MAX; ++bu) v |= bm[bu * nbw + w];
+    uni[w] = v;
   }
   __syncthreads();
   if (tid == 0) {
@@ -1410,7 +1414,7 @@ void k_apply_pair(const int64_t *__restrict__ row_ptr, const int32_t *__restrict
   __syncthreads();
 
   // ---- per-wave constants ---------------------------------------------------
-  const int a = wave % kPairT, part = wave / kPairT;    // target slot, 64-row part
+  const int a = wave % TP, part = wave / TP;           // target slot, 64-row part
   const int ta = uni32(stgt[a]);
   const int nsa = uni32(sns[a]);
   const int r32 = lane & 31;
@@ -1454,14 +1458,15 @@ void k_apply_pair(const int64_t *__restrict__ row_ptr, const int32_t *__restrict
   const int boff = C::V_OFF + a * C::V_BYTES + lane * 16;
 
   // load pieces, moved straight from memory to LDS (each load instruction of a
-  // wave fills 64 consecutive 16-byte LDS positions).  Source piece i of a
-  // lane: slot i, position tid of the slot, in query block qw (uniform per
-  // wave).  V piece j: target slot v_slot[j] (uniform), position r of its slice.
-  const int srow = 32 * (tid >> 6) + (tid & 31), shalf = (tid >> 5) & 1;
-  const int qw = uni32(srow / B);                      // query block of this wave's source pieces
-  const int srow_in = srow % B;
-  const int p_goff = (srow_in >> 4) * (B / 32) * 1024 + (shalf * 16 + (srow_in & 15)) * 16;
-  const int p_lds = wave * 1024;                       // the wave's block inside a slot
+  // wave fills 64 consecutive 16-byte LDS positions).  A wave loads, for SPW
+  // slots, every 32-row block of one query block qw: piece (slot wq * SPW + i,
+  // block kb) lands at block qw * NBQ + kb of the slot.  V piece j: target
+  // slot v_slot[j] (uniform), position r of its slice.
+  const int qw = wave / C::WQ, wq = wave % C::WQ;
+  // within a tile, a step's 16 keys of rows 16 g .. 16 g + 15 are 512 bytes at
+  // g * (B / 32) * 1024 + s * 512, key half h of row r at (16 h + r % 16) * 16
+  const int p_goff = ((r32 >> 4) * (B / 32) * 1024) + ((lane >> 5) * 16 + (r32 & 15)) * 16;
+  constexpr int KB_STRIDE = 2 * (B / 32) * 1024;      // between 32-row blocks of a tile
   int v_slot[VP], v_goff[VP], v_lds[VP];
 #pragma unroll
   for (int j = 0; j < VP; ++j) {
@@ -1475,26 +1480,26 @@ void k_apply_pair(const int64_t *__restrict__ row_ptr, const int32_t *__restrict
   int v_head[VP];  // V head of each V piece's target (-1: no target, or past the slices)
 #pragma unroll
   for (int j = 0; j < VP; ++j) {
-    const int t = v_slot[j] < kPairT ? uni32(stgt[v_slot[j]]) : -1;
+    const int t = v_slot[j] < TP ? uni32(stgt[v_slot[j]]) : -1;
     v_head[j] = t >= 0 ? t / grp : -1;
   }
   const int64_t vhead_elems = (int64_t)NBR * B * D;
   const int nsteps = nblk * KS;
 
-  // per key block: descriptors of the tiles of the wave's source pieces (slot
-  // i of query block qw) and of the V block of its V pieces
+  // per key block: descriptors of the tiles of the wave's source pieces (one
+  // per slot, query block qw) and of the V block of its V pieces
   struct Desc {
-    __amdgpu_buffer_rsrc_t t[SP];
+    __amdgpu_buffer_rsrc_t t[SPW];
     __amdgpu_buffer_rsrc_t v[VP];
   };
   auto make_desc = [&](Desc &dd, int k) {
     const bool valid = k < nblk;
     const int kk = valid ? (desc ? nblk - 1 - k : k) : 0;
     const int J = uni32(blist[kk]);
-    // lane i < U: tile index of slot i of query block qw at J, or -1
+    // lane u < U: tile index of slot u of query block qw at J, or -1
     int ti = -1;
     if (valid && lane < U && (qw == 0 || has1)) {
-      const int bu = qw * kPairU + lane;
+      const int bu = qw * U_MAX + lane;
       const uint32_t wd = bm[bu * nbw + (J >> 5)];
       if ((wd >> (J & 31)) & 1u) {
         const int64_t x = rbase[bu] + pc[bu * nbw + (J >> 5)] + __popc(wd & ((1u << (J & 31)) - 1u));
@@ -1502,8 +1507,8 @@ void k_apply_pair(const int64_t *__restrict__ row_ptr, const int32_t *__restrict
       }
     }
 #pragma unroll
-    for (int i = 0; i < SP; ++i) {
-      const int tix = __builtin_amdgcn_readlane(ti, i);
+    for (int i = 0; i < SPW; ++i) {
+      const int tix = __builtin_amdgcn_readlane(ti, wq * SPW + i);
       dd.t[i] = __builtin_amdgcn_make_buffer_rsrc(
           (void *)(tiles + uni64((int64_t)(tix >= 0 ? tix : 0) * TBYTES)), 0,
           tix >= 0 ? (int)TBYTES : 0, kBufferFlags);
@@ -1520,14 +1525,16 @@ void k_apply_pair(const int64_t *__restrict__ row_ptr, const int32_t *__restrict
   // step s of a block: every piece of the wave, memory -> LDS stage
   auto dma = [&](char *stage, const Desc &dd, int s) {
 #pragma unroll
-    for (int i = 0; i < SP; ++i)
-      lds_load16<0>(dd.t[i], stage + i * C::SRC_BYTES + p_lds, p_goff, s * 512);
+    for (int i = 0; i < SPW; ++i)
+#pragma unroll
+      for (int kb = 0; kb < NBQ; ++kb)
+        lds_load16<0>(dd.t[i], stage + (wq * SPW + i) * C::SRC_BYTES + (qw * NBQ + kb) * 1024,
+                      p_goff, s * 512 + kb * KB_STRIDE);
 #pragma unroll
     for (int j = 0; j < VP; ++j)
-      if (v_slot[j] < kPairT)
+      if (v_slot[j] < TP)
         lds_load16<kPairVPolicy>(dd.v[j], stage + v_lds[j], v_goff[j], s * C::V_BYTES);
   };
-
   f32x16 acc[RB][NB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
@@ -1582,16 +1589,14 @@ void k_apply_pair(const int64_t *__restrict__ row_ptr, const int32_t *__restrict
     dma(st0, dc, 0);
     step_end();
     for (int k = 0; k < nblk; ++k) {
-      // steps s, s + 1 of block k, each prefetching the next step into the
-      // other stage; the last step of a block prefetches the next block's first
+      // step s of block k: the next step (the next block's first after the
+      // last) moves into the other stage while step s is computed
 #pragma unroll
-      for (int s = 0; s < KS; s += 2) {
-        dma(st1, dc, s + 1);
-        compute(st0);
-        step_end();
-        if (s + 2 == KS) make_desc(dc, k + 1);
-        dma(st0, dc, (s + 2) % KS);
-        compute(st1);
+      for (int s = 0; s < KS; ++s) {
+        char *cur = (s & 1) ? st1 : st0, *nxt = (s & 1) ? st0 : st1;
+        if (s + 1 == KS) make_desc(dc, k + 1);
+        dma(nxt, dc, (s + 1) % KS);
+        compute(cur);
         step_end();
       }
     }
@@ -1636,24 +1641,25 @@ static mf_status launch_apply_fmt(hipStream_t s, const mf_bsr_map *map, const fl
   const char *tiles = static_cast<const char *>(map->tiles);
   const int64_t npos = ((int64_t)nrows + kXcds - 1) / kXcds * kXcds;
   if constexpr (FMT == MF_TILE_BF16) {
-    using CP = PairCfg<B, D>;
-    const size_t smem_pair = (size_t)pair_tables<B, D>(nbw).total;
+    using CP = PairCfg<B, D, kPairT>;
+    const size_t smem_pair = (size_t)pair_tables<B, D, kPairT>(nbw).total;
     if (smem_pair > 160 * 1024) return MF_ERR_UNSUPPORTED;
-    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&k_apply_pair<B, D>),
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&k_apply_pair<B, D, kPairT>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem_pair) != hipSuccess)
       return MF_ERR_HIP;
     int32_t *gtab = at<int32_t>(ws, w.gtab);
-    hipLaunchKernelGGL(k_pairs, dim3(1), dim3(64), 0, s, W, Ht, map->num_heads, gtab);
+    hipLaunchKernelGGL(k_pairs, dim3(1), dim3(64), 0, s, W, Ht, map->num_heads,
+                       (int32_t)(kPairT == 2), gtab);
     if (hip_status() != MF_OK) return MF_ERR_HIP;
     // any two targets with at most four sources fit one work-group
-    const int32_t ngmax = (Ht + 1) / 2;
+    const int32_t ngmax = (Ht + kPairT - 1) / kPairT;
     const int64_t nppos = ((int64_t)npairs + kXcds - 1) / kXcds * kXcds;
     if (npairs > 0)
-      hipLaunchKernelGGL((k_apply_pair<B, D>), dim3((unsigned)(nppos * ngmax)), dim3(CP::NT),
-                         smem_pair, s, map->row_ptr, map->col_idx, tiles, map->kept_mass,
-                         map->num_heads, g.NBR, g.T, W, Ht / Hkv, at<uint16_t>(ws, w.vt),
-                         at<RowInfo>(ws, w.rt.rows), psched, npairs, nbw, map->capacity_tiles,
-                         renorm, o, map->row_alias, gtab, ngmax);
+      hipLaunchKernelGGL((k_apply_pair<B, D, kPairT>), dim3((unsigned)(nppos * ngmax)),
+                         dim3(CP::NT), smem_pair, s, map->row_ptr, map->col_idx, tiles,
+                         map->kept_mass, map->num_heads, g.NBR, g.T, W, Ht / Hkv,
+                         at<uint16_t>(ws, w.vt), at<RowInfo>(ws, w.rt.rows), psched, npairs, nbw,
+                         map->capacity_tiles, renorm, o, map->row_alias, gtab, ngmax);
   } else {
     if (smem + vbufs > 64 * 1024 &&
         hipFuncSetAttribute(reinterpret_cast<const void *>(&k_apply4<B, D, FMT>),
