@@ -105,24 +105,41 @@ def mfma_flops(torch, wl, m, W, nnz: int) -> dict:
     return dict(compress=compress, apply=2.0 * s.B * s.B * s.d * blocks)
 
 
-def cpu_baseline(wl, rows):
-    """The fp64 oracle on a bounded sample of block-rows (all heads, all targets),
-    scaled to the whole workload by the share of causal key blocks the sample covers."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, rows, target_stride: int = 2):
+    """The fp64 oracle on a bounded sample: block-rows `rows` compressed for every
+    source head, retrieved for every `target_stride`-th target head; each part
+    scaled to the whole workload (compress by the share of causal key blocks the
+    sampled rows cover, retrieval also by the share of targets)."""
     from threadpoolctl import threadpool_info
     from oracle import mapflow_oracle as orc
     s = wl.spec
+    targets = list(range(0, s.Ht, target_stride))
     t0 = time.perf_counter()
     res = orc.compress(wl.q, wl.k, wl.cu_seqlens, s.B, s.p, wl.bias(), rows=rows)
-    orc.apply(res, wl.W, wl.v, wl.cu_seqlens, s.B, s.Hkv, rows=rows)
-    dt = time.perf_counter() - t0
+    t1 = time.perf_counter()
+    orc.apply(res, wl.W, wl.v, wl.cu_seqlens, s.B, s.Hkv, rows=rows, targets=targets)
+    t2 = time.perf_counter()
     blocks_sample = sum(I + 1 for (_, I) in rows)
     blocks_total = sum(n * (n + 1) // 2 for n in ((L + s.B - 1) // s.B for L in wl.lens))
-    full = dt * blocks_total / blocks_sample
+    full = ((t1 - t0) + (t2 - t1) * s.Ht / len(targets)) * blocks_total / blocks_sample
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     return dict(value=wl.T / full, unit="tokens/s", cores=int(threads), kind="oracle",
-                sample=(f"fp64 numpy oracle, compress + apply of block-rows {[I for _, I in rows]} "
-                        f"(all {s.Hs} source / {s.Ht} target heads) in {dt:.1f} s, scaled by "
-                        f"{blocks_total}/{blocks_sample} causal key blocks to the whole workload"))
+                cpu=cpu_model(),
+                sample=(f"fp64 numpy oracle: compress of block-rows {[I for _, I in rows]} (all {s.Hs} "
+                        f"source heads, {t1 - t0:.1f} s) and retrieval of them for {len(targets)} of "
+                        f"{s.Ht} target heads ({t2 - t1:.1f} s), scaled by {s.Ht}/{len(targets)} targets "
+                        f"and {blocks_total}/{blocks_sample} causal key blocks to the whole workload; "
+                        f"BLAS uses up to {threads} threads, numpy's elementwise exp and sums one"))
 
 
 def copy_calibration(torch, nbytes: int = 1 << 30, reps: int = 3):
@@ -392,8 +409,10 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        nb = (wl.lens[0] + s.B - 1) // s.B
-        rows = [(0, nb - 1), (0, nb // 2)]
+        # 8 block-rows at the centres of 8 equal bands of the longest sequence
+        sq = int(np.argmax(wl.lens))
+        nb = (wl.lens[sq] + s.B - 1) // s.B
+        rows = sorted({(sq, min(nb - 1, int((2 * b + 1) * nb // 16))) for b in range(8)})
         log(f"cpu baseline on block-rows {rows} ...")
         cpu = cpu_baseline(wl, rows)
         log(f"cpu baseline {cpu['value']:.1f} tokens/s")

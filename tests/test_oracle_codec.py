@@ -180,3 +180,48 @@ def test_apply_row_codec_exact_on_grid_and_bounded():
 def test_apply_rejects_unknown_codec():
     with pytest.raises(ValueError):
         orc.apply_row({}, np.zeros((1, 1)), 0, np.zeros((4, 2)), 32, codec="int4")
+
+
+def _grid_from_bits():
+    """All finite non-negative E4M3 values, decoded here from the bit layout
+    (exponent field f, mantissa m: f = 0 -> m/8 * 2^-6, else (1 + m/8) * 2^(f-7);
+    0x7F is NaN), independently of mx.e4m3_value."""
+    vals = []
+    for code in range(0x7F):
+        f, m = code >> 3, code & 7
+        vals.append(m / 8.0 * 2.0 ** -6 if f == 0 else (1.0 + m / 8.0) * 2.0 ** (f - 7))
+    return np.array(sorted(vals))
+
+
+@pytest.mark.parametrize("E", [7, 0, -5, -30])
+def test_error_bound_is_the_grid_half_spacing(E):
+    """error_bound pinned against the E4M3 grid by brute force: in a block whose
+    maximum lies in [2^E, 2^(E+1)) (scale e = E - 7), every element p = y 2^e
+    rounds to within half the local grid spacing of y; the worst case is the
+    midpoint of two neighbours.  At every midpoint the bound must cover that
+    half spacing (validity), and it must not be loose: it is attained exactly on
+    the subnormal part of the grid and within a factor 1 + 1/16 at the bottom of
+    every normal binade (tightness), so a looser or tighter formula fails."""
+    g = _grid_from_bits()
+    assert len(g) == 127 and g[0] == 0.0 and g[-1] == 448.0
+    e = E - 7
+    # scaled values of such a block lie in [0, 256): neighbours up to 256
+    g = g[g <= 256.0]
+    lo, hi = g[:-1], g[1:]
+    mid = (lo + hi) / 2
+    half = (hi - lo) / 2
+    # one block per midpoint: the midpoint and a maximum 1.5 * 2^E that fixes the scale
+    P = np.zeros((len(mid), 32))
+    P[:, 0] = mid * 2.0 ** e
+    P[:, 1] = 1.5 * 2.0 ** E
+    assert all(mx.block_scale_exponent(a) == e for a in P.max(axis=1))
+    bound = mx.error_bound(P)[:, 0]
+    worst = half * 2.0 ** e
+    assert np.all(worst <= bound), "the bound misses the rounding error at a midpoint"
+    ratio = worst / bound
+    sub = hi <= 2.0 ** -6                       # both neighbours on the subnormal spacing
+    assert np.allclose(ratio[sub], 1.0)
+    assert ratio[~sub].max() == pytest.approx(1.0 / (1.0 + 1.0 / 16), rel=1e-12)
+    # the codec really reaches the half spacing there (ties round to even)
+    q = mx.quantize(P)[:, 0]
+    assert np.allclose(np.abs(q - P[:, 0]), worst)
