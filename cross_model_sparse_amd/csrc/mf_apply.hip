@@ -148,13 +148,13 @@ __global__ __launch_bounds__(1024) void k_window_sched(const RowInfo *__restrict
 // per (target, query block) set-up shared by both apply kernels
 // ---------------------------------------------------------------------------
 // Dynamic LDS (byte offsets; the V buffers are static): rbase[Hs] int64,
-// src[Hs], wt[Hs], bm[Hs][nbw], pc[Hs][nbw], uni[nbw], coef[Hs][B] (bf16 bits), nsrc.
+// src[Hs], wt[Hs], bm[Hs][nbw], pc[Hs][nbw], uni[nbw], coef[Hs][B] (fp32), nsrc.
 // k_apply4 appends the union's key-block list: blist[nbw * 32] int32 and
 // tix[nbw * 32][4] int32 (tile index of each of up to four sources, -1 if none).
 inline size_t apply_smem(int B, int Hs, int nbw) {
   size_t s = (size_t)Hs * (8 + 4 + 4);
   s += (size_t)Hs * nbw * 8 + (size_t)nbw * 4;
-  s += (size_t)Hs * B * 2;
+  s += (size_t)Hs * B * 4;
   s += 64;
   s += (size_t)nbw * 32 * 5 * 4;
   return s;
@@ -168,7 +168,7 @@ struct RowMaps {
   uint32_t *bm;     // kept bitmaps [source][nbw]
   int32_t *pc;      // exclusive popcount prefix of bm (tile rank of each word)
   uint32_t *uni;    // union of the kept bitmaps
-  uint16_t *coef;   // [source][B] row coefficients W[t,h] / kmass_h[i], bf16 bits
+  float *coef;      // [source][B] row coefficients W[t,h] / kmass_h[i]
   int32_t *nsrc;
   int32_t *tix;     // [k][4] tile index of source u at the k-th union block, -1 if none
   int32_t *blist;   // [k] the k-th key block of the union, ascending
@@ -184,7 +184,7 @@ __device__ __forceinline__ RowMaps row_maps(char *smem, int Hs, int nbw, int B) 
   const int o_pc = o_bm + Hs * nbw * 4;
   const int o_uni = o_pc + Hs * nbw * 4;
   const int o_coef = o_uni + nbw * 4;
-  const int o_ns = (o_coef + Hs * B * 2 + 3) & ~3;
+  const int o_ns = o_coef + Hs * B * 4;
   const int o_tix = (o_ns + 4 + 15) & ~15;
   const int o_blist = o_tix + nbw * 32 * 16;
   RowMaps m;
@@ -194,7 +194,7 @@ __device__ __forceinline__ RowMaps row_maps(char *smem, int Hs, int nbw, int B) 
   m.bm = reinterpret_cast<uint32_t *>(smem + o_bm);
   m.pc = reinterpret_cast<int32_t *>(smem + o_pc);
   m.uni = reinterpret_cast<uint32_t *>(smem + o_uni);
-  m.coef = reinterpret_cast<uint16_t *>(smem + o_coef);
+  m.coef = reinterpret_cast<float *>(smem + o_coef);
   m.nsrc = reinterpret_cast<int32_t *>(smem + o_ns);
   m.tix = reinterpret_cast<int32_t *>(smem + o_tix);
   m.blist = reinterpret_cast<int32_t *>(smem + o_blist);
@@ -231,7 +231,7 @@ __device__ int row_sources(const RowMaps &m, const float *__restrict__ W, int t,
 }
 
 // Kept bitmaps of the ns sources at block-row gr, their tile ranks, the union
-// bitmap and the per-row coefficients (bf16): W[t,h] / kmass_h[i] when
+// bitmap and the per-row coefficients (fp32): W[t,h] / kmass_h[i] when
 // renormalising (0 where the kept mass is 0), else W[t,h]; rows past the
 // sequence end get 0.
 template <int B, int NT>
@@ -259,7 +259,7 @@ __device__ void row_maps_fill(const RowMaps &m, int ns, const int64_t *__restric
         c = m.wt[q];
       }
     }
-    m.coef[q * B + il] = (uint16_t)pack_bf16x2(c, 0.f);
+    m.coef[q * B + il] = c;
   }
   __syncthreads();
   for (int q = tid; q < ns; q += NT) {
@@ -490,7 +490,8 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(4))) void
   for (int h = 0; h < RG; ++h)
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      clo[h][u] = u < ns ? (uint32_t)mp.coef[u * B + wave * 16 * RG + 16 * h + m16] : 0u;
+      clo[h][u] = u < ns ? pack_bf16x2(mp.coef[u * B + wave * 16 * RG + 16 * h + m16], 0.f) & 0xffffu
+                         : 0u;
 
   const int nblk = build_block_list<C::NT>(mp, ns, n, capacity, tid);
 
@@ -558,10 +559,10 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(4))) void
 #pragma unroll
     for (int nb = 0; nb < D / 16; ++nb) acc[h][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // fp8: coefficients as fp32, scaled per chunk by the tile's block scale
+  // fp8: coefficients in fp32, scaled per chunk by the tile's block scale
   float cf[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) cf[u] = __uint_as_float(clo[0][u] << 16);
+  for (int u = 0; u < 4; ++u) cf[u] = u < ns ? mp.coef[u * B + wave * 16 * RG + m16] : 0.f;
 
   if (nblk > 0) {
     // queue of tile descriptors: S[k] for the (cur + k)-th union block

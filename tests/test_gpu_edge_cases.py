@@ -144,3 +144,72 @@ def test_zero_kept_mass_rows(gpu, idx, kw, W_kind, fmt):
     err = check_apply(O, out, wl.cu_seqlens, B)
     say(f"kept mass 0: {len(all_zero)} rows all sources, {len(one_zero)} rows source {h1}; "
         f"{W_kind} W {fmt}: out_err={err:.2e}")
+
+
+def _bf16_round(x: np.ndarray) -> np.ndarray:
+    """float32 -> nearest-even bf16 value, as float64."""
+    b = wlmod.f32_to_bf16_bits(np.asarray(x, dtype=np.float32)).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def _retrieval_with_bf16_coefficients(res, W, v, cu, B, Hkv, codec=None):
+    """The oracle's retrieval step with each coefficient W[t,h] / kmass_h[i] first
+    formed in fp32 and rounded to bf16, the way the dense-mixing kernel holds it
+    (a model of that kernel's rounding, used only to size its share)."""
+    from oracle import mx_codec
+    Ht = W.shape[0]
+    out = {}
+    for t in range(Ht):
+        g = orc.v_head(t, Ht, Hkv)
+        for (h, s, I), rr in res.items():
+            if W[t, h] == 0.0:
+                continue
+            a, L = orc.seqs(cu)[s]
+            vs = np.asarray(v[g, a:a + L], dtype=np.float64)
+            inv = np.where(rr.kmass > 0, np.float32(1.0) / rr.kmass.astype(np.float32), np.float32(0.0))
+            c = _bf16_round(np.float32(W[t, h]) * inv.astype(np.float32))
+            acc = out.setdefault((t, s, I), np.zeros((len(rr.rows), vs.shape[1])))
+            for J in rr.kept:
+                blk = rr.P[:, J * B:(J + 1) * B]
+                if codec == "mxfp8":
+                    blk = mx_codec.quantize(rr.tile(J, B))[:blk.shape[0], :blk.shape[1]]
+                acc += c[:, None] * (blk @ vs[J * B:J * B + blk.shape[1]])
+    return out
+
+
+@pytest.mark.parametrize("idx,lens,kw,fmt", [
+    (2, [900, 130], dict(Hs=12, Ht=8, Hkv=8), "bf16"),
+    (3, [1000], dict(Hs=12, Ht=16, Hkv=4), "bf16"),
+    (5, [600, 640, 65], dict(Hs=16, Ht=16, Hkv=16), "bf16"),
+    (5, [600, 640, 65], dict(Hs=16, Ht=16, Hkv=16), "mxfp8"),
+])
+def test_dense_mixing_coefficient_rounding_share(gpu, idx, lens, kw, fmt):
+    """The dense-mixing kernel (more than four sources per target) holds each
+    coefficient W[t,h] / kmass_h[i] in bf16 for its paired dot products.  Sized
+    here per workload (dense Gaussian W, mixed signs): the relative Frobenius
+    distance that this rounding alone puts between the exact oracle and the
+    oracle with rounded coefficients, next to the GPU's own error; the rounding
+    must stay under half the 1e-2 output budget."""
+    wl = wlmod.small_variant(idx, lens, **kw)
+    B = wl.spec.B
+    assert (np.count_nonzero(wl.W, axis=1) > 4).all()
+    m, st, nnz = gpu_compress(wl, gpu, tile_format=fmt)
+    assert st == mf.MF_OK
+    res = orc.compress(wl.q, wl.k, wl.cu_seqlens, B, wl.spec.p, wl.bias())
+    stats = check_rows(HostMap(m), res, wl.cu_seqlens, wl.T)
+    res = regrade(res, stats["overrides"])
+    codec = "mxfp8" if fmt == "mxfp8" else None
+    O = mf.mf_apply_translated(m, torch.from_numpy(wl.W).to(gpu), to_dev_v(wl, gpu),
+                               wl.cu_seqlens).cpu().numpy()
+    exact = orc.apply(res, wl.W, wl.v, wl.cu_seqlens, B, wl.spec.Hkv, codec=codec)
+    model = _retrieval_with_bf16_coefficients(res, wl.W, wl.v, wl.cu_seqlens, B, wl.spec.Hkv, codec)
+    Om = np.zeros_like(O)
+    for (t, s, I), blk in model.items():
+        a = int(wl.cu_seqlens[s]) + I * B
+        Om[t, a:a + blk.shape[0]] = blk
+    e_gpu = check_apply(O, exact, wl.cu_seqlens, B)
+    e_coef = check_apply(Om, exact, wl.cu_seqlens, B)
+    e_rest = check_apply(O, model, wl.cu_seqlens, B)
+    say(f"dense mixing {wl.spec.name[:20]} {fmt}: GPU vs exact {e_gpu:.2e}; bf16 coefficients alone "
+        f"{e_coef:.2e}; GPU vs rounded-coefficient model {e_rest:.2e}")
+    assert e_coef <= 0.5e-2

@@ -596,8 +596,9 @@ def _receiver_dev(rq, rk, rqb, rkb, dev):
     (5, [300, 520, 64, 1, 129, 0, 700], dict(Hs=4, Ht=4, Hkv=4), 2, "mxfp8"),
 ])
 def test_tv_distance_small(gpu, idx, lens, kw, Hkr, fmt):
-    """Per-row TV distance against the oracle on every block-row (rows at an
-    ambiguous top-p cut excluded), with receiver heads sharing K heads (GQA)."""
+    """Per-row TV distance against the oracle on every block-row (a row that flips
+    at an ambiguous top-p cut graded on the GPU's own kept set), with receiver
+    heads sharing K heads (GQA)."""
     wl = wlmod.make_config(1) if lens is None else wlmod.small_variant(idx, lens, **kw)
     B = wl.spec.B
     say(f"tv {wl.spec.name} lens={wl.lens[:8]} Hkr={Hkr} tiles={fmt}")
@@ -609,13 +610,10 @@ def test_tv_distance_small(gpu, idx, lens, kw, Hkr, fmt):
     tv = mf.mf_tv_distance(m, Wt, qd, kd, wl.cu_seqlens, wl.bias()).cpu().numpy()
     res = orc.compress(wl.q, wl.k, wl.cu_seqlens, B, wl.spec.p, wl.bias())
     stats = check_rows(HostMap(m), res, wl.cu_seqlens, wl.T)
-    flips = {(s, I) for (h, s, I) in stats["flips"]}
-    ref = orc.tv_distance(res, wl.W, rq, rk, wl.cu_seqlens, B, wl.bias(),
+    ref = orc.tv_distance(regrade(res, stats["overrides"]), wl.W, rq, rk, wl.cu_seqlens, B, wl.bias(),
                           codec="mxfp8" if fmt == "mxfp8" else None)
     worst, mean = 0.0, []
     for (t, s, I), v in ref.items():
-        if (s, I) in flips:
-            continue
         a = int(wl.cu_seqlens[s]) + I * B
         g = tv[t, a:a + len(v)]
         e = float(np.max(np.abs(g - v))) if len(v) else 0.0
@@ -623,7 +621,8 @@ def test_tv_distance_small(gpu, idx, lens, kw, Hkr, fmt):
         mean.append(v)
         assert e <= _tv_tol(wl.W, t), f"tv {(t, s, I)}: max error {e}"
     mean = float(np.concatenate(mean).mean())
-    say(f"  max |tv - oracle| {worst:.2e}, mean tv {mean:.3f}, flipped block-rows {len(flips)}")
+    say(f"  max |tv - oracle| {worst:.2e}, mean tv {mean:.3f}, flipped rows {stats['ambiguous_rows']} "
+        f"(graded on the GPU's sets)")
     assert 0.0 < mean < 1.5
 
 
@@ -706,12 +705,12 @@ def test_paged_chunked_equals_plain(gpu, idx, lens, kw, P, fmt):
     win = chunks[min(1, len(chunks) - 1)]
     rows = [(s, I) for s, (a, b) in enumerate(win) for I in range(a // B, (b + B - 1) // B)]
     res = orc.compress(wl.q, wl.k, wl.cu_seqlens, B, wl.spec.p, wl.bias(), rows=rows)
-    out = orc.apply(res, wl.W, wl.v, wl.cu_seqlens, B, wl.spec.Hkv, rows=rows,
-                    codec="mxfp8" if fmt == "mxfp8" else None)
     hm = HostMap(m, rows=[h * m.num_block_rows + global_row(wl.cu_seqlens, B, s, I)
                           for h in range(wl.spec.Hs) for (s, I) in rows])
     stats = check_rows(hm, res, wl.cu_seqlens, wl.T)
-    err = check_apply(O2.cpu().numpy(), out, wl.cu_seqlens, B, {(s, I) for (h, s, I) in stats["flips"]})
+    out = orc.apply(regrade(res, stats["overrides"]), wl.W, wl.v, wl.cu_seqlens, B, wl.spec.Hkv,
+                    rows=rows, codec="mxfp8" if fmt == "mxfp8" else None)
+    err = check_apply(O2.cpu().numpy(), out, wl.cu_seqlens, B)
     say(f"paged P={P} {fmt}: {len(chunks)} chunks, rows {len(rows)} of chunk 1 vs oracle {err:.2e}")
 
 
