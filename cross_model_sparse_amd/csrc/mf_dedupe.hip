@@ -15,7 +15,13 @@
 //   k_chain      per sequence: the block hashes chained from block 0, so equal
 //                chain values mean equal whole prefixes;
 //   k_alias      per block-row: the first earlier sequence whose same block-row
-//                is full and has the same chain value.
+//                is full and has the same chain value (a candidate);
+//   k_verify     the hash is only a filter: consecutive block-rows of a sequence
+//                whose candidates are consecutive block-rows of one earlier
+//                sequence form a run, and the last row of each run compares its
+//                whole prefix (every head, q and k) with the candidate's byte
+//                for byte, which covers every row of the run;
+//   k_alias_fix  a run with any differing byte keeps its own rows.
 #include "mf_host.hpp"
 
 namespace mf {
@@ -50,9 +56,11 @@ __global__ __launch_bounds__(256) void k_blockhash(const char *__restrict__ q,
                                                    int32_t Hs, int32_t rowbytes, int32_t B,
                                                    const RowInfo *__restrict__ rows,
                                                    Hash128 *__restrict__ hash,
-                                                   int32_t *__restrict__ full) {
+                                                   int32_t *__restrict__ full,
+                                                   int32_t *__restrict__ mism) {
   __shared__ uint64_t sa[256], sb[256];
   const int gr = blockIdx.x, tid = threadIdx.x;
+  if (tid == 0) mism[gr] = 0;  // byte mismatch flag of the verify pass
   const RowInfo ri = rows[gr];
   const bool is_full = (int64_t)(ri.blk + 1) * B <= ri.len;
   if (!is_full) {
@@ -148,11 +156,73 @@ __global__ __launch_bounds__(256) void k_alias(const RowInfo *__restrict__ rows,
 }
 
 // ---------------------------------------------------------------------------
+// k_verify: grid (NBR, kVerifySplit); work-group (gr, part) takes a share of the
+// comparison if gr ends a run of candidates
+// ---------------------------------------------------------------------------
+constexpr int kVerifySplit = 64;
+
+__device__ __forceinline__ bool run_continues(const RowInfo *__restrict__ rows,
+                                              const int32_t *__restrict__ cand, int NBR, int gr) {
+  // row gr + 1 continues gr's run: same sequence, and its candidate is the next
+  // block-row of the same earlier sequence
+  return gr + 1 < NBR && cand[gr + 1] != gr + 1 && rows[gr + 1].seq == rows[gr].seq &&
+         cand[gr + 1] == cand[gr] + 1;
+}
+
+__global__ __launch_bounds__(256) void k_verify(const char *__restrict__ q,
+                                                const char *__restrict__ k, int64_t T,
+                                                int32_t Hs, int32_t rowbytes, int32_t B,
+                                                int32_t NBR, const RowInfo *__restrict__ rows,
+                                                const int32_t *__restrict__ cand,
+                                                int32_t *__restrict__ mism) {
+  const int gr = blockIdx.x, part = blockIdx.y, tid = threadIdx.x;
+  const int c = cand[gr];
+  if (c == gr || run_continues(rows, cand, NBR, gr)) return;
+  const RowInfo ri = rows[gr], rc = rows[c];
+  // tokens 0 .. (I + 1) B - 1 of both sequences, every head, q and k, 16-byte chunks
+  const int cpr = rowbytes / 16;
+  const int64_t ntok = (int64_t)(ri.blk + 1) * B;
+  const int64_t per_t = (int64_t)Hs * ntok * cpr;
+  bool diff = false;
+  for (int64_t x = (int64_t)part * 256 + tid; x < 2 * per_t; x += (int64_t)kVerifySplit * 256) {
+    const int tsel = x >= per_t;
+    const int64_t xx = x - tsel * per_t;
+    const int64_t h = xx / (ntok * cpr), rem = xx % (ntok * cpr);
+    const int64_t r = rem / cpr, col = rem % cpr;
+    const char *base = tsel ? k : q;
+    const u32x4 a = *reinterpret_cast<const u32x4 *>(base + (h * T + ri.start + r) * rowbytes + col * 16);
+    const u32x4 b = *reinterpret_cast<const u32x4 *>(base + (h * T + rc.start + r) * rowbytes + col * 16);
+    diff |= (a[0] != b[0]) | (a[1] != b[1]) | (a[2] != b[2]) | (a[3] != b[3]);
+  }
+  if (__any(diff) && (tid & 63) == 0) atomicOr(&mism[gr], 1);
+}
+
+// ---------------------------------------------------------------------------
+// k_alias_fix: one thread per global block-row; a candidate stands if its run
+// compared equal
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_alias_fix(const RowInfo *__restrict__ rows,
+                                                   const int32_t *__restrict__ cand,
+                                                   const int32_t *__restrict__ mism, int32_t NBR,
+                                                   int32_t *__restrict__ alias) {
+  const int gr = blockIdx.x * blockDim.x + threadIdx.x;
+  if (gr >= NBR) return;
+  const int c = cand[gr];
+  int out = gr;
+  if (c != gr) {
+    int e = gr;
+    while (run_continues(rows, cand, NBR, e)) ++e;
+    if (!mism[e]) out = c;
+  }
+  alias[gr] = out;
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 struct DedupeWs {
   RowTable rt;
-  size_t hash, chain, full;
+  size_t hash, chain, full, cand, mism;
   size_t total;
 };
 
@@ -164,6 +234,8 @@ inline DedupeWs dedupe_ws(const SeqGeom &g) {
   w.hash = c.take<Hash128>(n);
   w.chain = c.take<Hash128>(n);
   w.full = c.take<int32_t>(n);
+  w.cand = c.take<int32_t>(n);
+  w.mism = c.take<int32_t>(n);
   w.total = c.off + 256;
   return w;
 }
@@ -199,14 +271,22 @@ extern "C" mf_status mf_prefix_dedupe(void *stream, const void *q, const void *k
   hipLaunchKernelGGL(k_blockhash, dim3(g.NBR), dim3(256), 0, s, static_cast<const char *>(q),
                      static_cast<const char *>(k), g.T, Hs, rowbytes, B,
                      at<RowInfo>(wsa, w.rt.rows), at<Hash128>(wsa, w.hash),
-                     at<int32_t>(wsa, w.full));
+                     at<int32_t>(wsa, w.full), at<int32_t>(wsa, w.mism));
   if (hip_status() != MF_OK) return MF_ERR_HIP;
   hipLaunchKernelGGL(k_chain, dim3((nseq + 255) / 256), dim3(256), 0, s,
                      at<int32_t>(wsa, w.rt.nbcum), nseq, at<Hash128>(wsa, w.hash),
                      at<int32_t>(wsa, w.full), at<Hash128>(wsa, w.chain));
   if (hip_status() != MF_OK) return MF_ERR_HIP;
+  int32_t *cand = at<int32_t>(wsa, w.cand);
   hipLaunchKernelGGL(k_alias, dim3((g.NBR + 255) / 256), dim3(256), 0, s,
                      at<RowInfo>(wsa, w.rt.rows), at<int32_t>(wsa, w.rt.nbcum), cu_dev, g.NBR, B,
-                     at<Hash128>(wsa, w.chain), at<int32_t>(wsa, w.full), row_alias);
+                     at<Hash128>(wsa, w.chain), at<int32_t>(wsa, w.full), cand);
+  if (hip_status() != MF_OK) return MF_ERR_HIP;
+  hipLaunchKernelGGL(k_verify, dim3(g.NBR, kVerifySplit), dim3(256), 0, s,
+                     static_cast<const char *>(q), static_cast<const char *>(k), g.T, Hs, rowbytes,
+                     B, g.NBR, at<RowInfo>(wsa, w.rt.rows), cand, at<int32_t>(wsa, w.mism));
+  if (hip_status() != MF_OK) return MF_ERR_HIP;
+  hipLaunchKernelGGL(k_alias_fix, dim3((g.NBR + 255) / 256), dim3(256), 0, s,
+                     at<RowInfo>(wsa, w.rt.rows), cand, at<int32_t>(wsa, w.mism), g.NBR, row_alias);
   return hip_status();
 }
