@@ -66,7 +66,9 @@ __device__ __forceinline__ int64_t vs_index(int64_t NBR, int B, int D, int g, in
 template <int B, int D>
 __global__ __launch_bounds__(256) void k_vstage(VSrc vs, int64_t T,
                                                 const RowInfo *__restrict__ rows, int32_t NBR,
-                                                uint16_t *__restrict__ vt) {
+                                                uint16_t *__restrict__ vt,
+                                                const int32_t *__restrict__ need) {
+  if (need && *need == 0) return;  // no kernel of this call reads the staged V
   constexpr int P = B + 8;  // LDS row pitch in elements
   __shared__ __attribute__((aligned(16))) uint16_t t[D * P];
   const int gr = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
@@ -355,6 +357,7 @@ __device__ __forceinline__ void mix_word(float &even, float &odd, uint32_t w, ui
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glob_void;
 
 // One 16-byte piece per lane, memory -> LDS: the wave's 64 pieces land at
 // lds + 16 * lane.
@@ -1063,12 +1066,14 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(2))) void
 // more than four sources are left to k_apply_mix.
 //
 // gtab[0] = number of groups; group q holds targets gtab[1 + 2q], gtab[2 + 2q]
-// (-1 for an empty slot).  With pair == 0 every such target forms a group of
-// its own.  One wave; Ht <= kMaxTargets, Hs <= kMixMaxSources.
+// (-1 for an empty slot); gtab[kMixFlag] = 1 if some target has more than four
+// sources (k_apply_mix has work), else 0.  With pair == 0 every such target
+// forms a group of its own.  One wave; Ht <= kMaxTargets, Hs <= kMixMaxSources.
 // ---------------------------------------------------------------------------
 constexpr int kPairT = 2;          // targets per work-group of the translated retrieval
 constexpr int kMaxTargets = 1024;
 constexpr int kMixMaxSources = 128;
+constexpr int kMixFlag = 1 + 2 * kMaxTargets;
 
 __global__ __launch_bounds__(64) void k_pairs(const float *__restrict__ W, int32_t Ht, int32_t Hs,
                                               int32_t pair, int32_t *__restrict__ gtab) {
@@ -1085,6 +1090,12 @@ __global__ __launch_bounds__(64) void k_pairs(const float *__restrict__ W, int32
     state[t] = cnt <= 4 ? 0 : 2;
   }
   __syncthreads();
+  {
+    bool mix = false;
+    for (int t = lane; t < Ht; t += 64) mix |= state[t] == 2;
+    const uint64_t any = wave_ballot(mix);
+    if (lane == 0) gtab[kMixFlag] = any != 0ull ? 1 : 0;
+  }
   auto wave_min = [](int v) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
@@ -1133,10 +1144,13 @@ __global__ __launch_bounds__(1024) void k_pair_sched(const RowInfo *__restrict__
                                                      const int32_t *__restrict__ sched,
                                                      int32_t NBR, int32_t B,
                                                      const int32_t *__restrict__ window,
-                                                     int32_t *__restrict__ psched) {
+                                                     int32_t *__restrict__ psched,
+                                                     u32x4 *__restrict__ vzero) {
   __shared__ int32_t wsum[16];
   __shared__ int32_t base;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the zero V row the retrieval reads past a sequence's end (1 KB)
+  if (tid < 64) vzero[tid] = u32x4{0u, 0u, 0u, 0u};
   if (tid == 0) base = 0;
   __syncthreads();
   for (int p0 = 0; p0 < NBR; p0 += 1024) {
@@ -1266,8 +1280,8 @@ template <int B, int D, int TP>
 __global__ __launch_bounds__((PairCfg<B, D, TP>::NT)) __attribute__((amdgpu_waves_per_eu(2)))
 void k_apply_pair(const int64_t *__restrict__ row_ptr, const int32_t *__restrict__ col_idx,
                   const char *__restrict__ tiles, const float *__restrict__ kept_mass, int32_t Hs,
-                  int32_t NBR, int64_t T, const float *__restrict__ W, int32_t grp,
-                  const uint16_t *__restrict__ vt, const RowInfo *__restrict__ rows,
+                  int32_t NBR, int64_t T, const float *__restrict__ W, int32_t grp, VSrc vs,
+                  const char *__restrict__ vzero, const RowInfo *__restrict__ rows,
                   const int32_t *__restrict__ psched, int32_t npairs, int32_t nbw,
                   int64_t capacity, int32_t renorm, float *__restrict__ o,
                   const int32_t *__restrict__ row_alias, const int32_t *__restrict__ gtab,
@@ -1305,6 +1319,7 @@ void k_apply_pair(const int64_t *__restrict__ row_ptr, const int32_t *__restrict
   grq[1] = uni32(psched[2 * pidx + 1]);
   const RowInfo r0 = rows[grq[0]];
   const int L = uni32(r0.len);
+  const int seq = uni32(r0.seq);
   const int64_t tok0 = (int64_t)uni32(r0.start);
   Iq[0] = uni32(r0.blk);
   Iq[1] = Iq[0] - 1;                                   // partner (if any) is the block below
@@ -1456,7 +1471,7 @@ void k_apply_pair(const int64_t *__restrict__ row_ptr, const int32_t *__restrict
   int aoff[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) aoff[rb] = (2 * part + rb) * 1024 + lane * 16;
-  const int boff = C::V_OFF + a * C::V_BYTES + lane * 16;
+  const int boff = C::V_OFF + a * C::V_BYTES + (lane >> 5) * 8 * (D * 2) + r32 * NB * 2;
 
   // load pieces, moved straight from memory to LDS (each load instruction of a
   // wave fills 64 consecutive 16-byte LDS positions).  A wave loads, for SPW
@@ -1468,30 +1483,81 @@ void k_apply_pair(const int64_t *__restrict__ row_ptr, const int32_t *__restrict
   // g * (B / 32) * 1024 + s * 512, key half h of row r at (16 h + r % 16) * 16
   const int p_goff = ((r32 >> 4) * (B / 32) * 1024) + ((lane >> 5) * 16 + (r32 & 15)) * 16;
   constexpr int KB_STRIDE = 2 * (B / 32) * 1024;      // between 32-row blocks of a tile
-  int v_slot[VP], v_goff[VP], v_lds[VP];
+  // V: each target's 16-key slice of a step sits in LDS token-major (16 rows of
+  // D bf16), read straight from V (contiguous or through the page table).  A
+  // 1 KB piece is TPP tokens; piece p of the step (p = wave + NW j) belongs to
+  // target slot p / PPT, tokens TPP (p % PPT) ...; lane l takes 16 bytes of
+  // token l / CPT of the piece.
+  constexpr int CPT = D * 2 / 16;                      // 16-byte chunks of a token row
+  constexpr int TPP = 64 / CPT;                        // tokens of a 1 KB piece
+  constexpr int PPT = C::V_BYTES / 1024;               // pieces of a target's slice
+  int v_slot[VP], v_lds[VP], v_tok0[VP], v_head[VP];
 #pragma unroll
   for (int j = 0; j < VP; ++j) {
-    const int p = tid + C::NT * j;
-    v_slot[j] = uni32(p / (2 * D));
-    const int r = p % (2 * D);
-    const int d = 32 * (r >> 6) + (r & 31), half = (r >> 5) & 1;
-    v_goff[j] = (d * 2 + half) * 16;                   // staged V chunk: column d, key half
-    v_lds[j] = uni32(C::V_OFF + v_slot[j] * C::V_BYTES + (r - lane) * 16);
-  }
-  int v_head[VP];  // V head of each V piece's target (-1: no target, or past the slices)
-#pragma unroll
-  for (int j = 0; j < VP; ++j) {
+    const int p = wave + C::NW * j;
+    v_slot[j] = p / PPT;                               // >= TP: no piece
+    v_tok0[j] = TPP * (p % PPT);
+    v_lds[j] = C::V_OFF + v_slot[j] * C::V_BYTES + (p % PPT) * 1024;
     const int t = v_slot[j] < TP ? uni32(stgt[v_slot[j]]) : -1;
     v_head[j] = t >= 0 ? t / grp : -1;
   }
-  const int64_t vhead_elems = (int64_t)NBR * B * D;
+  const int v_chunk = (lane % CPT) * 16;
+  // contiguous V: one buffer descriptor per piece over the sequence's rows of
+  // its head (zero length for an absent target), so rows past the sequence end
+  // read as zeros; the lane's offset is fixed, the step moves the scalar offset
+  __amdgpu_buffer_rsrc_t vdesc[VP];
+  int v_voff[VP];
+#pragma unroll
+  for (int j = 0; j < VP; ++j) {
+    const bool on = !vs.pages && v_slot[j] < TP && v_head[j] >= 0;
+    vdesc[j] = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(vs.v + uni64(on ? ((int64_t)v_head[j] * T + tok0) * D : 0)), 0, on ? L * D * 2 : 0,
+        kBufferFlags);
+    v_voff[j] = (v_tok0[j] + lane / CPT) * (D * 2) + v_chunk;
+  }
+  int vJ = 0;  // key block of the walk step being loaded (past the sequence: reads zeros)
+  // paged V: per key block, lane c < VP KS TPP holds the byte address of token row
+  // (piece j, step s, token tl), c = (j KS + s) TPP + tl: the row of V, or a
+  // zero row past the sequence end, for an absent target, a page outside the
+  // pool or a walk step past the last block
+  uint32_t va_lo = 0u, va_hi = 0u;
+  auto make_vaddr = [&](int k) {
+    const bool valid = k < nblk;
+    const int J = uni32(blist[valid ? (desc ? nblk - 1 - k : k) : 0]);
+    vJ = valid ? J : (L + B - 1) / B;
+    if (!vs.pages) return;
+    const char *row = vzero;
+    if (lane < VP * KS * TPP) {
+      const int jp = lane / (KS * TPP), st = (lane / TPP) % KS, tl = lane % TPP;
+      int g = -1, t0 = 0;
+#pragma unroll
+      for (int j = 0; j < VP; ++j)
+        if (j == jp) {
+          g = v_head[j];
+          t0 = v_tok0[j];
+        }
+      const int js = J * B + 16 * st + t0 + tl;        // token index inside the sequence
+      if (valid && g >= 0 && js < L) {
+        if (vs.pages) {
+          const int pg = vs.table[(int64_t)seq * vs.max_pages + js / vs.page_size];
+          if (pg >= 0 && pg < vs.num_pages)
+            row = reinterpret_cast<const char *>(
+                vs.pages + (((int64_t)pg * vs.Hkv + g) * vs.page_size + js % vs.page_size) * D);
+        } else {
+          row = reinterpret_cast<const char *>(vs.v + ((int64_t)g * T + tok0 + js) * D);
+        }
+      }
+    }
+    const uint64_t a = reinterpret_cast<uint64_t>(row);
+    va_lo = (uint32_t)a;
+    va_hi = (uint32_t)(a >> 32);
+  };
   const int nsteps = nblk * KS;
 
   // per key block: descriptors of the tiles of the wave's source pieces (one
   // per slot, query block qw) and of the V block of its V pieces
   struct Desc {
     __amdgpu_buffer_rsrc_t t[SPW];
-    __amdgpu_buffer_rsrc_t v[VP];
   };
   auto make_desc = [&](Desc &dd, int k) {
     const bool valid = k < nblk;
@@ -1514,14 +1580,6 @@ void k_apply_pair(const int64_t *__restrict__ row_ptr, const int32_t *__restrict
           (void *)(tiles + uni64((int64_t)(tix >= 0 ? tix : 0) * TBYTES)), 0,
           tix >= 0 ? (int)TBYTES : 0, kBufferFlags);
     }
-    const int64_t col0 = (int64_t)(grow0 + J) * B;      // first key column of the block
-#pragma unroll
-    for (int j = 0; j < VP; ++j) {
-      const bool on = valid && v_head[j] >= 0;
-      const int64_t off = uni64(on ? (int64_t)v_head[j] * vhead_elems + col0 * D : 0);
-      dd.v[j] = __builtin_amdgcn_make_buffer_rsrc((void *)(vt + off), 0, on ? B * D * 2 : 0,
-                                                  kBufferFlags);
-    }
   };
   // step s of a block: every piece of the wave, memory -> LDS stage
   auto dma = [&](char *stage, const Desc &dd, int s) {
@@ -1533,8 +1591,17 @@ void k_apply_pair(const int64_t *__restrict__ row_ptr, const int32_t *__restrict
                       p_goff, s * 512 + kb * KB_STRIDE);
 #pragma unroll
     for (int j = 0; j < VP; ++j)
-      if (v_slot[j] < TP)
-        lds_load16<kPairVPolicy>(dd.v[j], stage + v_lds[j], v_goff[j], s * C::V_BYTES);
+      if (v_slot[j] < TP) {
+        if (vs.pages) {
+          const int c = ((j * KS + s) * TPP + lane / CPT) * 4;
+          const uint64_t a = ((uint64_t)(uint32_t)__builtin_amdgcn_ds_bpermute(c, (int)va_hi) << 32) |
+                             (uint32_t)__builtin_amdgcn_ds_bpermute(c, (int)va_lo);
+          __builtin_amdgcn_global_load_lds((glob_void *)(a + v_chunk),
+                                           (lds_void *)(stage + v_lds[j]), 16, 0, 0);
+        } else {
+          lds_load16<0>(vdesc[j], stage + v_lds[j], v_voff[j], (vJ * B + 16 * s) * (D * 2));
+        }
+      }
   };
   f32x16 acc[RB][NB];
 #pragma unroll
@@ -1546,9 +1613,30 @@ void k_apply_pair(const int64_t *__restrict__ row_ptr, const int32_t *__restrict
   // first row block interleave with the mix of the second)
   auto compute = [&](const char *stage) {
     if (ta < 0) return;
+    // B operands from the token-major V slice: lane (h, m) reads, for its 8 keys
+    // 8 h .. 8 h + 7, the NB consecutive columns NB m .. NB m + NB - 1 (one 8- or
+    // 4-byte read per key; a half-wave reads one whole row), and v_perm_b32
+    // pairs consecutive keys of one column: operand e feeds the MFMA whose
+    // column n stands for value column NB n + e
+    uint32_t qd[8][NB / 2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const char *src = stage + boff + i * (D * 2);
+      if constexpr (NB == 4) {
+        const uint64_t x = *reinterpret_cast<const uint64_t *>(src);
+        qd[i][0] = (uint32_t)x;
+        qd[i][1] = (uint32_t)(x >> 32);
+      } else {
+        qd[i][0] = *reinterpret_cast<const uint32_t *>(src);
+      }
+    }
     u32x4 bv[NB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) bv[nb] = *reinterpret_cast<const u32x4 *>(stage + boff + nb * 1024);
+    for (int e = 0; e < NB; ++e)
+#pragma unroll
+      for (int pk = 0; pk < 4; ++pk)
+        bv[e][pk] = __builtin_amdgcn_perm(qd[2 * pk + 1][e >> 1], qd[2 * pk][e >> 1],
+                                          (e & 1) ? 0x07060302u : 0x05040100u);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       u32x4 v[4];
@@ -1587,6 +1675,7 @@ void k_apply_pair(const int64_t *__restrict__ row_ptr, const int32_t *__restrict
     char *st0 = smem, *st1 = smem + C::STAGE;
     Desc dc;
     make_desc(dc, 0);
+    make_vaddr(0);
     dma(st0, dc, 0);
     step_end();
     for (int k = 0; k < nblk; ++k) {
@@ -1595,7 +1684,10 @@ void k_apply_pair(const int64_t *__restrict__ row_ptr, const int32_t *__restrict
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         char *cur = (s & 1) ? st1 : st0, *nxt = (s & 1) ? st0 : st1;
-        if (s + 1 == KS) make_desc(dc, k + 1);
+        if (s + 1 == KS) {
+          make_desc(dc, k + 1);
+          make_vaddr(k + 1);
+        }
         dma(nxt, dc, (s + 1) % KS);
         compute(cur);
         step_end();
@@ -1614,9 +1706,15 @@ void k_apply_pair(const int64_t *__restrict__ row_ptr, const int32_t *__restrict
     for (int r = 0; r < 16; ++r) {
       const int ip = Iq[q] * B + (row0 % B) + acc_row(r, lane);
       if (ip < L) {
-        float *dst = ot + (tok0 + ip) * D + r32;
+        // value columns NB r32 .. NB r32 + NB - 1
+        float *dst = ot + (tok0 + ip) * D + NB * r32;
+        if constexpr (NB == 4) {
+          __builtin_nontemporal_store(f32x4{acc[rb][0][r], acc[rb][1][r], acc[rb][2][r], acc[rb][3][r]},
+                                      reinterpret_cast<f32x4 *>(dst));
+        } else {
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) __builtin_nontemporal_store(acc[rb][nb][r], dst + 32 * nb);
+          for (int nb = 0; nb < NB; ++nb) __builtin_nontemporal_store(acc[rb][nb][r], dst + nb);
+        }
       }
     }
   }
@@ -1630,11 +1728,12 @@ void k_apply_pair(const int64_t *__restrict__ row_ptr, const int32_t *__restrict
 // right after reading the weights.
 template <int B, int D, int FMT>
 static mf_status launch_apply_fmt(hipStream_t s, const mf_bsr_map *map, const float *W, int32_t Ht,
-                                  int32_t Hkv, const SeqGeom &g, int32_t renorm, float *o,
+                                  const VSrc &vs, const SeqGeom &g, int32_t renorm, float *o,
                                   void *ws, const VtWs &w, const int32_t *sched, int32_t nrows,
                                   const int32_t *psched, int32_t npairs, int nbw, size_t smem,
                                   size_t smem_mix, size_t vbufs, size_t vbufs_mix) {
   using CM = ApplyMixCfg<B, D, FMT>;
+  const int32_t Hkv = vs.Hkv;
   if (smem_mix + vbufs_mix > 64 * 1024 &&
       hipFuncSetAttribute(reinterpret_cast<const void *>(&k_apply_mix<B, D, FMT>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem_mix) != hipSuccess)
@@ -1648,18 +1747,15 @@ static mf_status launch_apply_fmt(hipStream_t s, const mf_bsr_map *map, const fl
     if (hipFuncSetAttribute(reinterpret_cast<const void *>(&k_apply_pair<B, D, kPairT>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem_pair) != hipSuccess)
       return MF_ERR_HIP;
-    int32_t *gtab = at<int32_t>(ws, w.gtab);
-    hipLaunchKernelGGL(k_pairs, dim3(1), dim3(64), 0, s, W, Ht, map->num_heads,
-                       (int32_t)(kPairT == 2), gtab);
-    if (hip_status() != MF_OK) return MF_ERR_HIP;
+    const int32_t *gtab = at<int32_t>(ws, w.gtab);
     // any two targets with at most four sources fit one work-group
     const int32_t ngmax = (Ht + kPairT - 1) / kPairT;
     const int64_t nppos = ((int64_t)npairs + kXcds - 1) / kXcds * kXcds;
     if (npairs > 0)
       hipLaunchKernelGGL((k_apply_pair<B, D, kPairT>), dim3((unsigned)(nppos * ngmax)),
                          dim3(CP::NT), smem_pair, s, map->row_ptr, map->col_idx, tiles,
-                         map->kept_mass, map->num_heads, g.NBR, g.T, W, Ht / Hkv,
-                         at<uint16_t>(ws, w.vt), at<RowInfo>(ws, w.rt.rows), psched, npairs, nbw,
+                         map->kept_mass, map->num_heads, g.NBR, g.T, W, Ht / Hkv, vs,
+                         at<char>(ws, w.vzero), at<RowInfo>(ws, w.rt.rows), psched, npairs, nbw,
                          map->capacity_tiles, renorm, o, map->row_alias, gtab, ngmax);
   } else {
     if (smem + vbufs > 64 * 1024 &&
@@ -1698,14 +1794,11 @@ static mf_status launch_apply(hipStream_t s, const mf_bsr_map *map, const float 
   const size_t vbufs = 2 * (size_t)B * D * 2;  // the two static V tile buffers of k_apply4
   const size_t vbufs_mix = (size_t)ApplyMixCfg<B, D, MF_TILE_BF16>::G * B * D * 2;
   if (smem + vbufs > 160 * 1024 || smem_mix + vbufs_mix > 160 * 1024) return MF_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL((k_vstage<B, D>), dim3(g.NBR, vs.Hkv), dim3(256), 0, s, vs, g.T,
-                     at<RowInfo>(ws, w.rt.rows), g.NBR, at<uint16_t>(ws, w.vt));
-  if (hip_status() != MF_OK) return MF_ERR_HIP;
   const int32_t *sched = at<int32_t>(ws, w.rt.sched);
   if (nrows == 0) return MF_OK;
   int32_t *psched = at<int32_t>(ws, w.psched);
   hipLaunchKernelGGL(k_pair_sched, dim3(1), dim3(1024), 0, s, at<RowInfo>(ws, w.rt.rows), sched,
-                     g.NBR, B, vs.window, psched);
+                     g.NBR, B, vs.window, psched, at<u32x4>(ws, w.vzero));
   if (hip_status() != MF_OK) return MF_ERR_HIP;
   if (vs.window) {
     hipLaunchKernelGGL(k_window_sched, dim3(1), dim3(1024), 0, s, at<RowInfo>(ws, w.rt.rows),
@@ -1713,11 +1806,24 @@ static mf_status launch_apply(hipStream_t s, const mf_bsr_map *map, const float 
     if (hip_status() != MF_OK) return MF_ERR_HIP;
     sched = at<int32_t>(ws, w.wsched);
   }
+  // bf16 maps: the target pairs, and whether any target is left to the
+  // dense-mixing kernel; only that kernel and the fp8 one read the staged V
+  int32_t *gtab = at<int32_t>(ws, w.gtab);
+  const bool bf16 = map->tile_format != MF_TILE_MXFP8;
+  if (bf16) {
+    hipLaunchKernelGGL(k_pairs, dim3(1), dim3(64), 0, s, W, Ht, map->num_heads,
+                       (int32_t)(kPairT == 2), gtab);
+    if (hip_status() != MF_OK) return MF_ERR_HIP;
+  }
+  hipLaunchKernelGGL((k_vstage<B, D>), dim3(g.NBR, vs.Hkv), dim3(256), 0, s, vs, g.T,
+                     at<RowInfo>(ws, w.rt.rows), g.NBR, at<uint16_t>(ws, w.vt),
+                     bf16 ? gtab + kMixFlag : nullptr);
+  if (hip_status() != MF_OK) return MF_ERR_HIP;
   if (map->tile_format == MF_TILE_MXFP8)
-    return launch_apply_fmt<B, D, MF_TILE_MXFP8>(s, map, W, Ht, vs.Hkv, g, renorm, o, ws, w, sched,
+    return launch_apply_fmt<B, D, MF_TILE_MXFP8>(s, map, W, Ht, vs, g, renorm, o, ws, w, sched,
                                                  nrows, psched, npairs, nbw, smem, smem_mix, vbufs,
                                                  vbufs_mix);
-  return launch_apply_fmt<B, D, MF_TILE_BF16>(s, map, W, Ht, vs.Hkv, g, renorm, o, ws, w, sched,
+  return launch_apply_fmt<B, D, MF_TILE_BF16>(s, map, W, Ht, vs, g, renorm, o, ws, w, sched,
                                               nrows, psched, npairs, nbw, smem, smem_mix, vbufs,
                                               vbufs_mix);
 }

@@ -123,7 +123,7 @@ inline CompressWs compress_ws(const SeqGeom &g, int32_t Hs, int32_t B) {
 // schedule of a query window.
 struct VtWs {
   RowTable rt;
-  size_t vt, wsched, gtab, psched;
+  size_t vt, wsched, gtab, psched, vzero;
   size_t total;
 };
 
@@ -139,6 +139,7 @@ inline VtWs vt_ws(const SeqGeom &g, int32_t Hkv, int32_t B, int32_t d) {
   w.wsched = c.take<int32_t>(g.NBR > 0 ? g.NBR : 1);
   w.gtab = c.take<int32_t>(kGroupTableInts);
   w.psched = c.take<int32_t>(2 * (size_t)(g.NBR > 0 ? g.NBR : 1));
+  w.vzero = c.take<uint32_t>(256);  // 1 KB of zeros: the V row read past a sequence's end
   w.total = c.off + 256;
   return w;
 }
