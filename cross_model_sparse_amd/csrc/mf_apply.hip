@@ -391,6 +391,10 @@ __device__ __forceinline__ void dma_v_tile(char *dstbuf, const uint16_t *vtg, in
   }
 }
 
+// s_waitcnt immediate that waits until at most n vector-memory loads are
+// outstanding (expcnt and lgkmcnt left unconstrained)
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 template <int B>
 __device__ __forceinline__ u32x4 v_frag(const char *vl, int d, int c) {
   constexpr int CPR = B * 2 / 16;
@@ -716,40 +720,52 @@ struct ApplyMixCfg {
   static_assert(VINST * 1024 * NW == VBYTES, "V tile must split into 1 KB wave loads");
   static_assert(G * VBYTES <= 64 * 1024, "V buffers must stay in the first 64 KB of LDS");
 };
-// Dynamic LDS of k_apply_mix (byte offsets): src[Hs] int32, rbase[Hs] int64,
-// wtab[Hs][4] fp32 (weight of each source for each target of the group),
-// bm[Hs][nbw], pc[Hs][nbw], uni[nbw], rtab[Hs][B] fp32 (1 / kept mass of each
-// row, 0 where none), blist[nbw * 32], counters.
-inline size_t mix_smem(int B, int Hs, int nbw) {
-  size_t s = (size_t)Hs * (4 + 8 + 16);
+// Dynamic LDS of k_apply_mix (byte offsets): the V tiles [nvh][B * D] bf16
+// (nvh = most distinct V heads in one target group), then src[Hs] int32,
+// rbase[Hs] int64, wtab[Hs4][4] fp32 (weight of each source for each target of
+// the group), bm[Hs][nbw], pc[Hs][nbw], uni[nbw], rtab[Hs4][B] fp32 (1 / kept
+// mass of each row, 0 where none), ctab[Hs4 / 2][B][4] if used (bf16 maps: each
+// source pair's coefficient pair W[t,h] / kmass_h[i] per row and target, formed
+// once instead of in every chunk), blist[nbw * 32], counters.  The weight and
+// coefficient tables run to Hs4 = Hs rounded up to a whole source batch, zero
+// past the sources, so the mixing loop reads them without bounds tests.
+inline size_t mix_smem(int B, int D, int Hs, int nbw, int nvh, bool ctab) {
+  const size_t Hs4 = (size_t)(Hs + 3) / 4 * 4;
+  size_t s = (size_t)nvh * B * D * 2;
+  s += (size_t)Hs * (4 + 8) + Hs4 * 16;
   s += (size_t)Hs * nbw * 8 + (size_t)nbw * 4;
-  s += (size_t)Hs * B * 4;
+  s += Hs4 * B * 4;
+  if (ctab) s += Hs4 / 2 * B * 16;
   s += (size_t)nbw * 32 * 4;
   s += 64 + 64;
   return s;
 }
 
-template <int B, int D, int FMT>
+template <int B, int D, int FMT, bool CT>
 __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(2))) void k_apply_mix(
     const int64_t *__restrict__ row_ptr, const int32_t *__restrict__ col_idx,
     const char *__restrict__ tiles, const float *__restrict__ kept_mass, int32_t Hs,
     int32_t NBR, int64_t T, const float *__restrict__ W, int32_t Ht, int32_t grp,
     const uint16_t *__restrict__ vt, const RowInfo *__restrict__ rows,
     const int32_t *__restrict__ sched, int32_t nrows, int32_t nbw, int64_t capacity,
-    int32_t renorm, float *__restrict__ o, const int32_t *__restrict__ row_alias) {
+    int32_t renorm, float *__restrict__ o, const int32_t *__restrict__ row_alias, int32_t nvmax) {
   using C = ApplyMixCfg<B, D, FMT>;
   constexpr int G = C::G, KC = C::KC, SB = C::SB, NP = C::NP;
   constexpr bool FP8 = FMT == MF_TILE_MXFP8;
-  __shared__ __attribute__((aligned(16))) char vbuf[G * C::VBYTES];
+  constexpr int LPB = FP8 ? 2 * SB : SB;  // vector-memory loads per source batch
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const int o_src = 0;
+  char *vbuf = smem;  // first in LDS
+  const int o_src = nvmax * C::VBYTES;
   const int o_rbase = (o_src + Hs * 4 + 7) & ~7;
+  const int Hs4 = (Hs + 3) / 4 * 4;
+  static_assert(C::SB == 4, "tables are padded to whole batches of four sources");
   const int o_wt = o_rbase + Hs * 8;
-  const int o_bm = o_wt + Hs * 16;
+  const int o_bm = o_wt + Hs4 * 16;
   const int o_pc = o_bm + Hs * nbw * 4;
   const int o_uni = o_pc + Hs * nbw * 4;
   const int o_rt = o_uni + nbw * 4;
-  const int o_bl = o_rt + Hs * B * 4;
+  const int o_ct = o_rt + Hs4 * B * 4;
+  const int o_bl = o_ct + (CT ? Hs4 / 2 * B * 16 : 0);
   const int o_misc = o_bl + nbw * 32 * 4;
   int32_t *src = reinterpret_cast<int32_t *>(smem + o_src);
   int64_t *rbase = reinterpret_cast<int64_t *>(smem + o_rbase);
@@ -758,6 +774,7 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(2))) void
   int32_t *pc = reinterpret_cast<int32_t *>(smem + o_pc);
   uint32_t *uni = reinterpret_cast<uint32_t *>(smem + o_uni);
   float *rtab = reinterpret_cast<float *>(smem + o_rt);
+  u32x4 *ctab = reinterpret_cast<u32x4 *>(smem + o_ct);
   int32_t *blist = reinterpret_cast<int32_t *>(smem + o_bl);
   int32_t *misc = reinterpret_cast<int32_t *>(smem + o_misc);  // [0] ns, [1..G] active
 
@@ -827,6 +844,8 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(2))) void
   __syncthreads();
   const int ns = __builtin_amdgcn_readfirstlane(misc[0]);
   if (ns == 0) return;
+  const int ns4 = (ns + SB - 1) / SB * SB;  // whole batches; tables zero past ns
+  for (int i = ns * 4 + tid; i < ns4 * 4; i += C::NT) wtab[i] = 0.f;
   for (int q = 0; q < ns; ++q) {
     // entries past the capacity of an overflowed map are treated as missing
     const int64_t b0 = rbase[q], e0 = min(row_ptr[(int64_t)src[q] * NBR + grm + 1], capacity);
@@ -835,11 +854,11 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(2))) void
       atomicOr(&bm[q * nbw + (J >> 5)], 1u << (J & 31));
     }
   }
-  for (int idx = tid; idx < ns * B; idx += C::NT) {
+  for (int idx = tid; idx < ns4 * B; idx += C::NT) {
     const int q = idx / B, il = idx % B;
     const int ip = I * B + il;
     float r = 0.f;
-    if (ip < L) {
+    if (q < ns && ip < L) {
       if (renorm) {
         const float km = kept_mass[(int64_t)src[q] * T + tok0 + ip];
         r = km > 0.f ? 1.f / km : 0.f;
@@ -850,6 +869,20 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(2))) void
     rtab[q * B + il] = r;
   }
   __syncthreads();
+  if constexpr (CT) {
+    // coefficient pairs [c(2pq), c(2pq + 1)] of every source pair, row and
+    // target, in bf16 for v_dot2 (a missing second source: 0)
+    for (int idx = tid; idx < ns4 / 2 * B; idx += C::NT) {
+      const int pq = idx / B, il = idx % B;
+      const int u1 = 2 * pq, u2 = u1 + 1;
+      const float ra = rtab[u1 * B + il], rb = rtab[u2 * B + il];
+      u32x4 cq = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int g = 0; g < G; ++g) cq[g] = pack_bf16x2(wtab[u1 * 4 + g] * ra, wtab[u2 * 4 + g] * rb);
+      ctab[pq * B + il] = cq;
+    }
+    __syncthreads();
+  }
   const int nw_row = (n + 31) / 32;
   for (int q = tid; q < ns; q += C::NT) {
     int run = 0;
@@ -886,6 +919,9 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(2))) void
   for (int g = 0; g < G; ++g)
     if (t0 + g < Ht) nvh = (t0 + g) / grp - gv0 + 1;
 
+  int vho[G];  // LDS offset of each target's V tile (a target past Ht: any)
+#pragma unroll
+  for (int g = 0; g < G; ++g) vho[g] = min((t0 + g) / grp - gv0, nvh - 1) * C::VBYTES;
   const int r0 = wave * 16 + m16;                 // lane row inside the block
   // lane's bytes of chunk kc: bf16 16 bytes at loff + kc * 1024; fp8 8 bytes at
   // loff + (kc / NP) * 512 NP + (kc % NP) * 8, and its row's scale byte
@@ -897,6 +933,7 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(2))) void
 #pragma unroll
     for (int nb = 0; nb < D / 16; ++nb) acc[g][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  const int nst = KC * ((ns + SB - 1) / SB);  // source batches per key block
   for (int kb = 0; kb < nblk; ++kb) {
     const int J = __builtin_amdgcn_readfirstlane(blist[kb]);
     // tile index of every source at J, lane u holding sources u and u + 64
@@ -923,8 +960,8 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(2))) void
     for (int vh = 0; vh < nvh; ++vh)
       dma_v_tile<B, D, C::VINST>(vbuf + vh * C::VBYTES, vt + (int64_t)(gv0 + vh) * D * tpad, col0,
                                  wave, lane);
+    asm volatile("" ::: "memory");  // the V loads issue before this block's tile loads
 
-    u32x4 amix[G];
     // Buffer loads through one descriptor per source (wave-uniform base, 32-bit
     // lane offsets), zero-length for a source without a tile at this block, so
     // missing tiles read as zeros with no branch and no 64-bit lane addresses.
@@ -945,84 +982,78 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(2))) void
         }
       }
     };
+    // mix one batch of SB sources (u0 ..) into mx, two sources per v_dot2
+    auto mix_batch = [&](float (&mx)[G][8], const u32x4 (&cur)[SB], const uint32_t (&scur)[SB], int u0) {
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      float mx[G][8];
+      for (int pr = 0; pr < SB / 2; ++pr) {
+        const int u1 = u0 + 2 * pr, u2 = u1 + 1;
+        uint32_t cp[G];
+        if constexpr (CT) {
+          // the pair's coefficients from the table (zero past the sources)
+          const u32x4 cq = ctab[(u1 / 2) * B + r0];
 #pragma unroll
-      for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) mx[g][e] = 0.f;
-      u32x4 cur[SB], nxt[SB];
-      uint32_t scur[SB], snxt[SB];
-      load_batch(cur, scur, kc, 0);
-      for (int u0 = 0; u0 < ns; u0 += SB) {
-        if (u0 + SB < ns) load_batch(nxt, snxt, kc, u0 + SB);
-#pragma unroll
-        for (int pr = 0; pr < SB / 2; ++pr) {
-          const int u1 = u0 + 2 * pr, u2 = u1 + 1;
-          float ra = u1 < ns ? rtab[u1 * B + r0] : 0.f;
-          float rb = u2 < ns ? rtab[u2 * B + r0] : 0.f;
+          for (int g = 0; g < G; ++g) cp[g] = cq[g];
+        } else {
+          float ra = rtab[u1 * B + r0];
+          float rb = rtab[u2 * B + r0];
           if constexpr (FP8) {
             // the block scales 2^(byte - 127) folded into the coefficients
             ra = __builtin_amdgcn_ldexpf(ra, (int)scur[2 * pr] - 127);
             rb = __builtin_amdgcn_ldexpf(rb, (int)scur[2 * pr + 1] - 127);
           }
-          uint32_t cp[G];
 #pragma unroll
-          for (int g = 0; g < G; ++g) {
-            const float wa = u1 < ns ? wtab[u1 * 4 + g] : 0.f;
-            const float wb = u2 < ns ? wtab[u2 * 4 + g] : 0.f;
-            cp[g] = pack_bf16x2(wa * ra, wb * rb);
+          for (int g = 0; g < G; ++g) cp[g] = pack_bf16x2(wtab[u1 * 4 + g] * ra, wtab[u2 * 4 + g] * rb);
+        }
+        if constexpr (!FP8) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t lo = __builtin_amdgcn_perm(cur[2 * pr + 1][e], cur[2 * pr][e], 0x05040100u);
+            const uint32_t hi = __builtin_amdgcn_perm(cur[2 * pr + 1][e], cur[2 * pr][e], 0x07060302u);
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+              mx[g][2 * e] = __builtin_amdgcn_fdot2_f32_bf16(
+                  __builtin_bit_cast(bf16x2, lo), __builtin_bit_cast(bf16x2, cp[g]), mx[g][2 * e], false);
+              mx[g][2 * e + 1] = __builtin_amdgcn_fdot2_f32_bf16(
+                  __builtin_bit_cast(bf16x2, hi), __builtin_bit_cast(bf16x2, cp[g]), mx[g][2 * e + 1], false);
+            }
           }
-          if constexpr (!FP8) {
+        } else {
+          // byte pairs [P1[e], P2[e]] of the two sources' codes, then E4M3 ->
+          // bf16 (exact: 3 mantissa bits, and the scale 1 changes nothing)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const uint32_t lo = __builtin_amdgcn_perm(cur[2 * pr + 1][e], cur[2 * pr][e], 0x05040100u);
-              const uint32_t hi = __builtin_amdgcn_perm(cur[2 * pr + 1][e], cur[2 * pr][e], 0x07060302u);
+          for (int w = 0; w < 2; ++w)
 #pragma unroll
-              for (int g = 0; g < G; ++g) {
-                mx[g][2 * e] = __builtin_amdgcn_fdot2_f32_bf16(
-                    __builtin_bit_cast(bf16x2, lo), __builtin_bit_cast(bf16x2, cp[g]), mx[g][2 * e], false);
-                mx[g][2 * e + 1] = __builtin_amdgcn_fdot2_f32_bf16(
-                    __builtin_bit_cast(bf16x2, hi), __builtin_bit_cast(bf16x2, cp[g]), mx[g][2 * e + 1], false);
+            for (int hw = 0; hw < 2; ++hw) {
+              const uint32_t pairs = __builtin_amdgcn_perm(
+                  cur[2 * pr + 1][w], cur[2 * pr][w], hw ? 0x07030602u : 0x05010400u);
+              const bf16x2 pv[2] = {__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(pairs, 1.0f, false),
+                                    __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(pairs, 1.0f, true)};
+#pragma unroll
+              for (int k = 0; k < 2; ++k) {
+                const int e = 4 * w + 2 * hw + k;
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+                  mx[g][e] = __builtin_amdgcn_fdot2_f32_bf16(pv[k], __builtin_bit_cast(bf16x2, cp[g]),
+                                                             mx[g][e], false);
               }
             }
-          } else {
-            // byte pairs [P1[e], P2[e]] of the two sources' codes, then E4M3 ->
-            // bf16 (exact: 3 mantissa bits, and the scale 1 changes nothing)
-#pragma unroll
-            for (int w = 0; w < 2; ++w)
-#pragma unroll
-              for (int hw = 0; hw < 2; ++hw) {
-                const uint32_t pairs = __builtin_amdgcn_perm(
-                    cur[2 * pr + 1][w], cur[2 * pr][w], hw ? 0x07030602u : 0x05010400u);
-                const bf16x2 pv[2] = {__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(pairs, 1.0f, false),
-                                      __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(pairs, 1.0f, true)};
-#pragma unroll
-                for (int k = 0; k < 2; ++k) {
-                  const int e = 4 * w + 2 * hw + k;
-#pragma unroll
-                  for (int g = 0; g < G; ++g)
-                    mx[g][e] = __builtin_amdgcn_fdot2_f32_bf16(pv[k], __builtin_bit_cast(bf16x2, cp[g]),
-                                                               mx[g][e], false);
-                }
-              }
-          }
-        }
-#pragma unroll
-        for (int e = 0; e < SB; ++e) {
-          cur[e] = nxt[e];
-          scur[e] = snxt[e];
         }
       }
+    };
+    // chunk kc mixed: round to bf16 and multiply with V on MFMA
+    auto finish_chunk = [&](float (&mx)[G][8], int kc) {
+      u32x4 amix[G];
 #pragma unroll
       for (int g = 0; g < G; ++g)
 #pragma unroll
         for (int e = 0; e < 4; ++e) amix[g][e] = pack_bf16x2(mx[g][2 * e], mx[g][2 * e + 1]);
       if (kc == 0) {
-        // V tiles landed (direct-to-LDS loads: full drain) in every wave
+        // V tiles landed in every wave.  Vector-memory loads retire in issue
+        // order and the V loads went out before any tile load of this block, so
+        // allowing the two batches loaded after this one (LPB loads each) to
+        // stay in flight still covers them.
         asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LPB));
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
       }
@@ -1030,10 +1061,53 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(2))) void
       for (int nb = 0; nb < D / 16; ++nb)
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-          const int vh = (t0 + g < Ht) ? (t0 + g) / grp - gv0 : 0;
-          const u32x4 bv = v_frag<B>(vbuf + vh * C::VBYTES, nb * 16 + m16, kc * 4 + kg);
+          const u32x4 bv = v_frag<B>(vbuf + vho[g], nb * 16 + m16, kc * 4 + kg);
           acc[g][nb] = mfma16_bf16(as_bf16x8(amix[g]), as_bf16x8(bv), acc[g][nb]);
         }
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mx[g][e] = 0.f;
+    };
+
+    // The key block's KC * nsb source batches run as one stream through a ring
+    // of three register buffers: the batch two steps ahead loads while the
+    // current one is mixed, across the chunk boundary too.  The ring position
+    // is static (the loop is unrolled by three), so nothing is copied.  Every
+    // step issues its loads, past the last batch through zero-length
+    // descriptors, so the number of loads between a batch's issue and its use
+    // is fixed and the wait before the use is exact (a conditional load would
+    // make it a full drain).
+    float mx[G][8];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx[g][e] = 0.f;
+    u32x4 ring[3][SB];
+    uint32_t sring[3][SB];
+    int lkc = 0, lu0 = 0;  // next batch to load
+    auto next_load = [&](u32x4 (&d)[SB], uint32_t (&sb)[SB]) {
+      const bool past = lkc >= KC;  // sources from ns on have no tile: zero loads
+      load_batch(d, sb, past ? 0 : lkc, past ? ns : lu0);
+      lu0 += SB;
+      if (lu0 >= ns) { lu0 = 0; ++lkc; }
+    };
+    next_load(ring[0], sring[0]);
+    next_load(ring[1], sring[1]);
+    int ckc = 0, cu0 = 0;  // batch being mixed
+    for (int s0 = 0; s0 < nst; s0 += 3) {
+#pragma unroll
+      for (int r = 0; r < 3; ++r) {
+        if (s0 + r >= nst) break;
+        next_load(ring[(r + 2) % 3], sring[(r + 2) % 3]);
+        mix_batch(mx, ring[r], sring[r], cu0);
+        cu0 += SB;
+        if (cu0 >= ns) {
+          finish_chunk(mx, ckc);
+          cu0 = 0;
+          ++ckc;
+        }
+      }
     }
     // every wave's reads of V done before the next block's loads overwrite it
     __syncthreads();
@@ -1731,12 +1805,26 @@ static mf_status launch_apply_fmt(hipStream_t s, const mf_bsr_map *map, const fl
                                   const VSrc &vs, const SeqGeom &g, int32_t renorm, float *o,
                                   void *ws, const VtWs &w, const int32_t *sched, int32_t nrows,
                                   const int32_t *psched, int32_t npairs, int nbw, size_t smem,
-                                  size_t smem_mix, size_t vbufs, size_t vbufs_mix) {
+                                  size_t vbufs) {
   using CM = ApplyMixCfg<B, D, FMT>;
   const int32_t Hkv = vs.Hkv;
-  if (smem_mix + vbufs_mix > 64 * 1024 &&
-      hipFuncSetAttribute(reinterpret_cast<const void *>(&k_apply_mix<B, D, FMT>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem_mix) != hipSuccess)
+  // distinct V heads of a target group (the V tiles it holds in LDS)
+  int nvmax = 1;
+  for (int t0 = 0; t0 < Ht; t0 += CM::G) {
+    const int t1 = std::min(t0 + CM::G, (int)Ht) - 1;
+    nvmax = std::max(nvmax, t1 / (Ht / Hkv) - t0 / (Ht / Hkv) + 1);
+  }
+  // the coefficient table when it costs no occupancy (two work-groups per CU
+  // still fit, or not even one fits without it), else coefficients inline
+  const size_t mix_lo = mix_smem(B, D, map->num_heads, nbw, nvmax, false);
+  const size_t mix_hi = mix_smem(B, D, map->num_heads, nbw, nvmax, true);
+  const bool use_ct = FMT == MF_TILE_BF16 && mix_hi <= 160 * 1024 &&
+                      (mix_hi <= 80 * 1024 || mix_lo > 80 * 1024);
+  const size_t smem_mix = use_ct ? mix_hi : mix_lo;
+  const void *kmix = use_ct ? reinterpret_cast<const void *>(&k_apply_mix<B, D, FMT, FMT == MF_TILE_BF16>)
+                            : reinterpret_cast<const void *>(&k_apply_mix<B, D, FMT, false>);
+  if (smem_mix > 64 * 1024 &&
+      hipFuncSetAttribute(kmix, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem_mix) != hipSuccess)
     return MF_ERR_HIP;
   const char *tiles = static_cast<const char *>(map->tiles);
   const int64_t npos = ((int64_t)nrows + kXcds - 1) / kXcds * kXcds;
@@ -1770,11 +1858,18 @@ static mf_status launch_apply_fmt(hipStream_t s, const mf_bsr_map *map, const fl
   }
   if (hip_status() != MF_OK) return MF_ERR_HIP;
   const int64_t ngrp = (Ht + CM::G - 1) / CM::G;
-  hipLaunchKernelGGL((k_apply_mix<B, D, FMT>), dim3((unsigned)(npos * ngrp)), dim3(CM::NT),
-                     smem_mix, s, map->row_ptr, map->col_idx, tiles, map->kept_mass,
-                     map->num_heads, g.NBR, g.T, W, Ht, Ht / Hkv, at<uint16_t>(ws, w.vt),
-                     at<RowInfo>(ws, w.rt.rows), sched, nrows, nbw, map->capacity_tiles, renorm,
-                     o, map->row_alias);
+  auto launch_mix = [&](auto ct) {
+    constexpr bool CTB = decltype(ct)::value;
+    hipLaunchKernelGGL((k_apply_mix<B, D, FMT, CTB>), dim3((unsigned)(npos * ngrp)), dim3(CM::NT),
+                       smem_mix, s, map->row_ptr, map->col_idx, tiles, map->kept_mass,
+                       map->num_heads, g.NBR, g.T, W, Ht, Ht / Hkv, at<uint16_t>(ws, w.vt),
+                       at<RowInfo>(ws, w.rt.rows), sched, nrows, nbw, map->capacity_tiles, renorm,
+                       o, map->row_alias, nvmax);
+  };
+  if (use_ct)
+    launch_mix(std::integral_constant<bool, FMT == MF_TILE_BF16>{});
+  else
+    launch_mix(std::false_type{});
   return hip_status();
 }
 
@@ -1785,15 +1880,15 @@ static mf_status launch_apply(hipStream_t s, const mf_bsr_map *map, const float 
                               int32_t renorm, float *o, void *ws, const VtWs &w) {
   const int nbw = (g.maxnb + 31) / 32 > 0 ? (g.maxnb + 31) / 32 : 1;
   const size_t smem = apply_smem(B, map->num_heads, nbw);
-  const size_t smem_mix = mix_smem(B, map->num_heads, nbw);
   // tile indices are held in int32; V rows are addressed with 32-bit byte
   // offsets d * NBR * B * 2
   if (map->capacity_tiles > INT32_MAX) return MF_ERR_UNSUPPORTED;
   if ((int64_t)D * g.NBR * B * 2 >= ((int64_t)1 << 31)) return MF_ERR_UNSUPPORTED;
   if (map->num_heads > kMixMaxSources || Ht > kMaxTargets) return MF_ERR_UNSUPPORTED;
   const size_t vbufs = 2 * (size_t)B * D * 2;  // the two static V tile buffers of k_apply4
-  const size_t vbufs_mix = (size_t)ApplyMixCfg<B, D, MF_TILE_BF16>::G * B * D * 2;
-  if (smem + vbufs > 160 * 1024 || smem_mix + vbufs_mix > 160 * 1024) return MF_ERR_UNSUPPORTED;
+  if (smem + vbufs > 160 * 1024 ||
+      mix_smem(B, D, map->num_heads, nbw, ApplyMixCfg<B, D, MF_TILE_BF16>::G, false) > 160 * 1024)
+    return MF_ERR_UNSUPPORTED;
   const int32_t *sched = at<int32_t>(ws, w.rt.sched);
   if (nrows == 0) return MF_OK;
   int32_t *psched = at<int32_t>(ws, w.psched);
@@ -1821,11 +1916,9 @@ static mf_status launch_apply(hipStream_t s, const mf_bsr_map *map, const float 
   if (hip_status() != MF_OK) return MF_ERR_HIP;
   if (map->tile_format == MF_TILE_MXFP8)
     return launch_apply_fmt<B, D, MF_TILE_MXFP8>(s, map, W, Ht, vs, g, renorm, o, ws, w, sched,
-                                                 nrows, psched, npairs, nbw, smem, smem_mix, vbufs,
-                                                 vbufs_mix);
+                                                 nrows, psched, npairs, nbw, smem, vbufs);
   return launch_apply_fmt<B, D, MF_TILE_BF16>(s, map, W, Ht, vs, g, renorm, o, ws, w, sched,
-                                              nrows, psched, npairs, nbw, smem, smem_mix, vbufs,
-                                              vbufs_mix);
+                                              nrows, psched, npairs, nbw, smem, vbufs);
 }
 
 }  // namespace mf
