@@ -1057,13 +1057,25 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(2))) void
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
       }
+      // each 16-column slice: the G V fragments read together, then the MFMAs
+      // (fp8 maps, whose mixing holds more registers: one fragment at a time)
 #pragma unroll
-      for (int nb = 0; nb < D / 16; ++nb)
+      for (int nb = 0; nb < D / 16; ++nb) {
+        if constexpr (!FP8) {
+          u32x4 bq[G];
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const u32x4 bv = v_frag<B>(vbuf + vho[g], nb * 16 + m16, kc * 4 + kg);
-          acc[g][nb] = mfma16_bf16(as_bf16x8(amix[g]), as_bf16x8(bv), acc[g][nb]);
+          for (int g = 0; g < G; ++g) bq[g] = v_frag<B>(vbuf + vho[g], nb * 16 + m16, kc * 4 + kg);
+#pragma unroll
+          for (int g = 0; g < G; ++g)
+            acc[g][nb] = mfma16_bf16(as_bf16x8(amix[g]), as_bf16x8(bq[g]), acc[g][nb]);
+        } else {
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            const u32x4 bv = v_frag<B>(vbuf + vho[g], nb * 16 + m16, kc * 4 + kg);
+            acc[g][nb] = mfma16_bf16(as_bf16x8(amix[g]), as_bf16x8(bv), acc[g][nb]);
+          }
         }
+      }
 #pragma unroll
       for (int g = 0; g < G; ++g)
 #pragma unroll
