@@ -358,6 +358,12 @@ __device__ __forceinline__ void mix_word(float &even, float &odd, uint32_t w, ui
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glob_void;
+// global-memory views for loads from a wave-uniform base (selects the
+// base-in-SGPRs form of the global load)
+typedef __attribute__((address_space(1))) const unsigned char gchar;
+typedef __attribute__((address_space(1))) const u32x4 gu32x4;
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(1))) const u32x2_t gu32x2;
 
 // One 16-byte piece per lane, memory -> LDS: the wave's 64 pieces land at
 // lds + 16 * lane.
@@ -748,7 +754,8 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(2))) void
     int32_t NBR, int64_t T, const float *__restrict__ W, int32_t Ht, int32_t grp,
     const uint16_t *__restrict__ vt, const RowInfo *__restrict__ rows,
     const int32_t *__restrict__ sched, int32_t nrows, int32_t nbw, int64_t capacity,
-    int32_t renorm, float *__restrict__ o, const int32_t *__restrict__ row_alias, int32_t nvmax) {
+    int32_t renorm, float *__restrict__ o, const int32_t *__restrict__ row_alias, int32_t nvmax,
+    const char *__restrict__ zbuf) {
   using C = ApplyMixCfg<B, D, FMT>;
   constexpr int G = C::G, KC = C::KC, SB = C::SB, NP = C::NP;
   constexpr bool FP8 = FMT == MF_TILE_MXFP8;
@@ -937,24 +944,25 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(2))) void
   for (int kb = 0; kb < nblk; ++kb) {
     const int J = __builtin_amdgcn_readfirstlane(blist[kb]);
     // tile index of every source at J, lane u holding sources u and u + 64
-    int ti[2];
+    // as the tile's address (two 32-bit halves); a source without a tile at J,
+    // or past the union, points at the zero block
+    uint32_t tlo[2], thi[2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const int u = lane + 64 * hh;
-      int v = -1;
+      const char *a = zbuf;
       if (u < ns) {
         const uint32_t word = bm[u * nbw + (J >> 5)];
         if ((word >> (J & 31)) & 1u) {
           const int64_t tix = rbase[u] + pc[u * nbw + (J >> 5)] + __popc(word & ((1u << (J & 31)) - 1u));
-          if (tix < capacity) v = (int)tix;
+          if (tix < capacity) a = tiles + tix * C::TBYTES;
         }
       }
-      ti[hh] = v;
+      tlo[hh] = (uint32_t)reinterpret_cast<uintptr_t>(a);
+      thi[hh] = (uint32_t)(reinterpret_cast<uintptr_t>(a) >> 32);
     }
-    auto tile_at = [&](int u) -> int {  // uniform
-      if (u >= ns) return -1;
-      return u < 64 ? __builtin_amdgcn_readlane(ti[0], u) : __builtin_amdgcn_readlane(ti[1], u - 64);
-    };
+    const uint32_t zlo = (uint32_t)reinterpret_cast<uintptr_t>(zbuf);
+    const uint32_t zhi = (uint32_t)(reinterpret_cast<uintptr_t>(zbuf) >> 32);
     // V tiles of this block for every distinct V head of the group
     const int64_t col0 = (int64_t)(gr - I + J) * B;
     for (int vh = 0; vh < nvh; ++vh)
@@ -962,23 +970,28 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(2))) void
                                  wave, lane);
     asm volatile("" ::: "memory");  // the V loads issue before this block's tile loads
 
-    // Buffer loads through one descriptor per source (wave-uniform base, 32-bit
-    // lane offsets), zero-length for a source without a tile at this block, so
-    // missing tiles read as zeros with no branch and no 64-bit lane addresses.
-    auto load_batch = [&](u32x4 (&d)[SB], uint32_t (&sb)[SB], int kc, int u0) {
+    // Loads from a wave-uniform 64-bit base (the tile, or the zero block for a
+    // missing tile, a source past the union or a batch past the block: `zero`)
+    // plus a 32-bit lane offset, so a missing tile costs no branch and no
+    // per-lane address arithmetic.
+    // A batch never straddles source 64 (batches start at multiples of SB), so
+    // its address pair is chosen once per batch, then read lane by lane.
+    auto load_batch = [&](u32x4 (&d)[SB], uint32_t (&sb)[SB], int kc, int u0, bool zero) {
+      const uint32_t blo = zero ? zlo : (u0 < 64 ? tlo[0] : tlo[1]);
+      const uint32_t bhi = zero ? zhi : (u0 < 64 ? thi[0] : thi[1]);
 #pragma unroll
       for (int e = 0; e < SB; ++e) {
-        const int t_ = tile_at(u0 + e);
-        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(tiles + (int64_t)(t_ >= 0 ? t_ : 0) * C::TBYTES), 0,
-            t_ >= 0 ? (int)C::TBYTES : 0, kBufferFlags);
+        const int l = (u0 + e) & 63;
+        const u32x2_t a2 = {(uint32_t)__builtin_amdgcn_readlane(blo, l), (uint32_t)__builtin_amdgcn_readlane(bhi, l)};
+        const gchar *tb = reinterpret_cast<const gchar *>(__builtin_bit_cast(uint64_t, a2));
         if constexpr (!FP8) {
-          d[e] = __builtin_amdgcn_raw_buffer_load_b128(r, loff, kc * 1024, 0);
+          d[e] = *reinterpret_cast<const gu32x4 *>(tb + (uint32_t)(loff + kc * 1024));
           sb[e] = 0u;
         } else {
-          const auto c2 = __builtin_amdgcn_raw_buffer_load_b64(r, loff, (kc / NP) * 512 * NP + (kc % NP) * 8, 0);
+          const auto c2 =
+              *reinterpret_cast<const gu32x2 *>(tb + (uint32_t)(loff + (kc / NP) * 512 * NP + (kc % NP) * 8));
           d[e] = u32x4{c2[0], c2[1], 0u, 0u};
-          sb[e] = __builtin_amdgcn_raw_buffer_load_b8(r, soff, kc, 0);
+          sb[e] = *(tb + (uint32_t)(soff + kc));
         }
       }
     };
@@ -1099,8 +1112,7 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(2))) void
     uint32_t sring[3][SB];
     int lkc = 0, lu0 = 0;  // next batch to load
     auto next_load = [&](u32x4 (&d)[SB], uint32_t (&sb)[SB]) {
-      const bool past = lkc >= KC;  // sources from ns on have no tile: zero loads
-      load_batch(d, sb, past ? 0 : lkc, past ? ns : lu0);
+      load_batch(d, sb, lkc < KC ? lkc : 0, lu0, lkc >= KC);
       lu0 += SB;
       if (lu0 >= ns) { lu0 = 0; ++lkc; }
     };
@@ -1235,8 +1247,9 @@ __global__ __launch_bounds__(1024) void k_pair_sched(const RowInfo *__restrict__
   __shared__ int32_t wsum[16];
   __shared__ int32_t base;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // the zero V row the retrieval reads past a sequence's end (1 KB)
-  if (tid < 64) vzero[tid] = u32x4{0u, 0u, 0u, 0u};
+  // the zero block: the V row the retrieval reads past a sequence's end, and
+  // the tile a source without one at some key block reads (kZeroBytes)
+  for (int i = tid; i < kZeroBytes / 16; i += 1024) vzero[i] = u32x4{0u, 0u, 0u, 0u};
   if (tid == 0) base = 0;
   __syncthreads();
   for (int p0 = 0; p0 < NBR; p0 += 1024) {
@@ -1876,7 +1889,7 @@ static mf_status launch_apply_fmt(hipStream_t s, const mf_bsr_map *map, const fl
                        smem_mix, s, map->row_ptr, map->col_idx, tiles, map->kept_mass,
                        map->num_heads, g.NBR, g.T, W, Ht, Ht / Hkv, at<uint16_t>(ws, w.vt),
                        at<RowInfo>(ws, w.rt.rows), sched, nrows, nbw, map->capacity_tiles, renorm,
-                       o, map->row_alias, nvmax);
+                       o, map->row_alias, nvmax, at<char>(ws, w.vzero));
   };
   if (use_ct)
     launch_mix(std::integral_constant<bool, FMT == MF_TILE_BF16>{});

@@ -127,6 +127,10 @@ struct VtWs {
   size_t total;
 };
 
+// Zero block of the apply workspace: at least one tile of the largest format
+// (B = 128 bf16) and one V row.
+constexpr int kZeroBytes = 32 * 1024;
+
 // Target-group table of the apply path: a count, then up to 1024 groups of at
 // most 4 targets.
 constexpr int kGroupTableInts = 1 + 4 * 1024;
@@ -139,7 +143,7 @@ inline VtWs vt_ws(const SeqGeom &g, int32_t Hkv, int32_t B, int32_t d) {
   w.wsched = c.take<int32_t>(g.NBR > 0 ? g.NBR : 1);
   w.gtab = c.take<int32_t>(kGroupTableInts);
   w.psched = c.take<int32_t>(2 * (size_t)(g.NBR > 0 ? g.NBR : 1));
-  w.vzero = c.take<uint32_t>(256);  // 1 KB of zeros: the V row read past a sequence's end
+  w.vzero = c.take<char>(kZeroBytes);  // zeros: a V row past a sequence's end, a missing tile
   w.total = c.off + 256;
   return w;
 }
