@@ -150,13 +150,17 @@ __global__ __launch_bounds__(1024) void k_window_sched(const RowInfo *__restrict
 // per (target, query block) set-up shared by both apply kernels
 // ---------------------------------------------------------------------------
 // Dynamic LDS (byte offsets; the V buffers are static): rbase[Hs] int64,
-// src[Hs], wt[Hs], bm[Hs][nbw], pc[Hs][nbw], uni[nbw], coef[Hs][B] (fp32), nsrc.
-// k_apply4 appends the union's key-block list: blist[nbw * 32] int32 and
-// tix[nbw * 32][4] int32 (tile index of each of up to four sources, -1 if none).
+// src[Hs], wt[Hs] (every source with a nonzero weight), then for the at most
+// kSrc4 sources k_apply4 mixes: bm[kSrc4][nbw], pc[kSrc4][nbw], uni[nbw],
+// coef[kSrc4][B] (fp32), nsrc.  k_apply4 appends the union's key-block list:
+// blist[nbw * 32] int32 and tix[nbw * 32][4] int32 (tile index of each of up
+// to four sources, -1 if none).  Sized for four sources, the tables leave room
+// for two work-groups per CU beside the two V tiles.
+constexpr int kSrc4 = 4;
 inline size_t apply_smem(int B, int Hs, int nbw) {
   size_t s = (size_t)Hs * (8 + 4 + 4);
-  s += (size_t)Hs * nbw * 8 + (size_t)nbw * 4;
-  s += (size_t)Hs * B * 4;
+  s += (size_t)kSrc4 * nbw * 8 + (size_t)nbw * 4;
+  s += (size_t)kSrc4 * B * 4;
   s += 64;
   s += (size_t)nbw * 32 * 5 * 4;
   return s;
@@ -183,10 +187,10 @@ __device__ __forceinline__ RowMaps row_maps(char *smem, int Hs, int nbw, int B) 
   const int o_src = o_rbase + Hs * 8;
   const int o_wt = o_src + Hs * 4;
   const int o_bm = o_wt + Hs * 4;
-  const int o_pc = o_bm + Hs * nbw * 4;
-  const int o_uni = o_pc + Hs * nbw * 4;
+  const int o_pc = o_bm + kSrc4 * nbw * 4;
+  const int o_uni = o_pc + kSrc4 * nbw * 4;
   const int o_coef = o_uni + nbw * 4;
-  const int o_ns = o_coef + Hs * B * 4;
+  const int o_ns = o_coef + kSrc4 * B * 4;
   const int o_tix = (o_ns + 4 + 15) & ~15;
   const int o_blist = o_tix + nbw * 32 * 16;
   RowMaps m;
@@ -227,7 +231,7 @@ __device__ int row_sources(const RowMaps &m, const float *__restrict__ W, int t,
     }
     if (tid == 0) *m.nsrc = ns;
   }
-  for (int i = tid; i < Hs * m.nbw; i += NT) m.bm[i] = 0u;
+  for (int i = tid; i < kSrc4 * m.nbw; i += NT) m.bm[i] = 0u;
   __syncthreads();
   return __builtin_amdgcn_readfirstlane(*m.nsrc);
 }
