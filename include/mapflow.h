@@ -234,8 +234,11 @@ mf_status mf_prefix_dedupe(void *stream, const void *q, const void *k, mf_dtype 
                            void *workspace, size_t workspace_bytes);
 
 /* Device workspace bytes mf_apply_translated and mf_apply_translated_paged need:
- * a block-padded copy of V staged in 16-key chunks ([Hkv][NBR * B / 16][d][16]
- * bf16), the block-row table and the query-block schedules.  0 if invalid. */
+ * room for a block-padded copy of V staged in 16-key chunks
+ * ([Hkv][NBR * B / 16][d][16] bf16; written only when some target has more
+ * than four sources or the map holds fp8 tiles, otherwise V is read in
+ * place), a 32 KB block the calls clear and read as zeros, the block-row table
+ * and the query-block schedules.  0 if invalid. */
 size_t mf_apply_workspace_bytes(int32_t Hkv, const int32_t *cu_seqlens_host, int32_t nseq,
                                 int32_t B, int32_t d);
 
