@@ -710,11 +710,11 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(4))) void
 // are c = W[t,h] / kmass_h[i] (bf16).
 //
 // Per key block of the union, the block's V tiles (one per distinct V head of
-// the group) load into LDS while the first 32-key chunk is mixed; then a full
-// drain and a barrier; then each chunk's bf16 mix is multiplied with V on MFMA
-// right after it is built; a barrier frees the V buffer for the next block.
-// Within a chunk, the next batch of source chunks loads while the current one
-// is mixed.
+// the group) load into LDS while the first 32-key chunk is mixed; a wait for
+// those loads and a barrier; then each chunk's bf16 mix is multiplied with V
+// on MFMA right after it is built; a barrier frees the V buffer for the next
+// block.  The source chunks stream through a three-batch register ring, two
+// batches ahead of the one being mixed.
 // ---------------------------------------------------------------------------
 template <int B, int D, int FMT>
 struct ApplyMixCfg {
