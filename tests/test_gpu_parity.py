@@ -119,6 +119,14 @@ def test_no_renorm_both_apply_kernels(gpu, idx, lens, kw, fmt):
     full_case(wlmod.small_variant(idx, lens, **kw), gpu, renorm=False, tile_format=fmt)
 
 
+@pytest.mark.parametrize("Hs,fmt", [(72, "bf16"), (70, "mxfp8")])
+def test_dense_mixing_past_64_sources(gpu, Hs, fmt):
+    """Dense W over more than 64 source heads: the mixing kernel's source union
+    spans both halves of its per-lane address table (sources 64 and up), and
+    70 is no whole number of four-source batches."""
+    full_case(wlmod.small_variant(2, [300, 70], Hs=Hs, Ht=4, Hkv=4), gpu, tile_format=fmt)
+
+
 def test_mixed_source_counts_and_partial_groups(gpu):
     """Targets with more than four sources (dense mixing) next to targets with four
     or fewer (sparse mixing) in one call; six targets, so the dense-mixing groups
