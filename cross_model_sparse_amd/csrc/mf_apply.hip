@@ -1614,8 +1614,8 @@ void k_apply_pair(const int64_t *__restrict__ row_ptr, const int32_t *__restrict
   for (int j = 0; j < VP; ++j) {
     const bool on = !vs.pages && v_slot[j] < TP && v_head[j] >= 0;
     vdesc[j] = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(vs.v + uni64(on ? ((int64_t)v_head[j] * T + tok0) * D : 0)), 0, on ? L * D * 2 : 0,
-        kBufferFlags);
+        (void *)(vs.v + uni64(on ? ((int64_t)v_head[j] * T + tok0) * D : 0)), 0,
+        uni32(on ? L * D * 2 : 0), kBufferFlags);
     v_voff[j] = (v_tok0[j] + lane / CPT) * (D * 2) + v_chunk;
   }
   int vJ = 0;  // key block of the walk step being loaded (past the sequence: reads zeros)
