@@ -25,6 +25,25 @@
 
 namespace mf {
 
+// Work-group id -> (schedule position, source head) of both passes.
+// Position-major by default: the work-groups in flight on one XCD are a run of
+// consecutive schedule positions for Hs / 8 heads, which in a single sequence
+// are neighbouring block-rows reading the same K rows.  Head-major (several
+// sequences, heads splitting evenly over the XCDs): each XCD takes its heads
+// one at a time, every position of a head before its next head, so that the
+// positions in flight, which the longest-first schedule draws from different
+// sequences, at least share one head's K rows in the XCD's L2.
+__device__ __forceinline__ void compress_slot(int b, int Hs, int NBR, int head_major, int &pos, int &h) {
+  if (head_major) {
+    const int x = b % kQkXcds, k = b / kQkXcds;
+    pos = k % NBR;
+    h = x + kQkXcds * (k / NBR);
+  } else {
+    pos = b / Hs;
+    h = b % Hs;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // k_select
 // ---------------------------------------------------------------------------
@@ -52,14 +71,15 @@ __global__ __launch_bounds__(B * 2) __attribute__((amdgpu_waves_per_eu(SelectCfg
     const int64_t *__restrict__ pbase, int64_t ptot, float scale2, BiasArgs bias, double p,
     float *__restrict__ lse2_out, float *__restrict__ partials, int32_t *__restrict__ counts,
     uint32_t *__restrict__ bitmaps, int32_t nbw, float *__restrict__ kept_mass,
-    const int32_t *__restrict__ row_alias) {
+    const int32_t *__restrict__ row_alias, int32_t head_major) {
   using C = QKCfg<B, D, F32>;
   using E = std::conditional_t<F32, float, uint16_t>;
   __shared__ __attribute__((aligned(16))) char smem[SelectCfg<B, D, F32>::SMEM];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int m = lane & 31, hl = lane >> 5;
-  const int pos = blockIdx.x / Hs, h = blockIdx.x % Hs;
+  int pos, h;
+  compress_slot(blockIdx.x, Hs, NBR, head_major, pos, h);
   const int gr = sched[pos];
   if (row_alias && row_alias[gr] != gr && row_alias[gr] >= 0 && row_alias[gr] < NBR) {
     // shares an earlier block-row: no tiles of its own (kept mass is copied
@@ -400,7 +420,7 @@ __global__ __launch_bounds__(B * 2) __attribute__((amdgpu_waves_per_eu(F32 ? 1 :
     const RowInfo *__restrict__ rows, const int32_t *__restrict__ sched, float scale2,
     BiasArgs bias, const float *__restrict__ lse2_in, const uint32_t *__restrict__ bitmaps,
     int32_t nbw, const int64_t *__restrict__ row_ptr, int64_t capacity,
-    int32_t *__restrict__ col_idx, char *__restrict__ tiles) {
+    int32_t *__restrict__ col_idx, char *__restrict__ tiles, int32_t head_major) {
   using C = QKCfg<B, D, F32>;
   using TC = TilesCfg<B, D, F32>;
   using E = std::conditional_t<F32, float, uint16_t>;
@@ -410,7 +430,8 @@ __global__ __launch_bounds__(B * 2) __attribute__((amdgpu_waves_per_eu(F32 ? 1 :
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int m = lane & 31, hl = lane >> 5;
-  const int pos = blockIdx.x / Hs, h = blockIdx.x % Hs;
+  int pos, h;
+  compress_slot(blockIdx.x, Hs, NBR, head_major, pos, h);
   const int gr = sched[pos];
   const RowInfo ri = rows[gr];
   const int I = ri.blk, L = ri.len;
@@ -520,12 +541,13 @@ static mf_status launch_compress(hipStream_t s, const void *q, const void *k, co
                                  void *ws, const CompressWs &w) {
   const float scale2 = kLog2e / sqrtf((float)D);
   const int64_t ptot = (int64_t)B * g.tri;
+  const int32_t head_major = (Hs % kQkXcds == 0 && g.nseq > 1) ? 1 : 0;
   const dim3 grid((unsigned)((int64_t)g.NBR * Hs));
   hipLaunchKernelGGL((k_select<B, D, F32>), grid, dim3(B * 2), 0, s, q, k, g.T, Hs, g.NBR,
                      at<RowInfo>(ws, w.rt.rows), at<int32_t>(ws, w.rt.sched),
                      at<int64_t>(ws, w.rt.pbase), ptot, scale2, ba, p, at<float>(ws, w.lse2),
                      at<float>(ws, w.partials), at<int32_t>(ws, w.counts),
-                     at<uint32_t>(ws, w.bitmaps), w.nbw, map->kept_mass, map->row_alias);
+                     at<uint32_t>(ws, w.bitmaps), w.nbw, map->kept_mass, map->row_alias, head_major);
   if (hip_status() != MF_OK) return MF_ERR_HIP;
   if (map->row_alias) {
     hipLaunchKernelGGL(k_alias_kmass, dim3(g.NBR), dim3(256), 0, s, at<RowInfo>(ws, w.rt.rows),
@@ -541,12 +563,12 @@ static mf_status launch_compress(hipStream_t s, const void *q, const void *k, co
     hipLaunchKernelGGL((k_tiles<B, D, F32, MF_TILE_MXFP8>), grid, dim3(B * 2), 0, s, q, k, g.T,
                        Hs, g.NBR, at<RowInfo>(ws, w.rt.rows), at<int32_t>(ws, w.rt.sched),
                        scale2, ba, at<float>(ws, w.lse2), at<uint32_t>(ws, w.bitmaps), w.nbw,
-                       map->row_ptr, map->capacity_tiles, map->col_idx, tiles);
+                       map->row_ptr, map->capacity_tiles, map->col_idx, tiles, head_major);
   else
     hipLaunchKernelGGL((k_tiles<B, D, F32, MF_TILE_BF16>), grid, dim3(B * 2), 0, s, q, k, g.T,
                        Hs, g.NBR, at<RowInfo>(ws, w.rt.rows), at<int32_t>(ws, w.rt.sched),
                        scale2, ba, at<float>(ws, w.lse2), at<uint32_t>(ws, w.bitmaps), w.nbw,
-                       map->row_ptr, map->capacity_tiles, map->col_idx, tiles);
+                       map->row_ptr, map->capacity_tiles, map->col_idx, tiles, head_major);
   return hip_status();
 }
 

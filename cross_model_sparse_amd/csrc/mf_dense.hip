@@ -115,11 +115,31 @@ __device__ __forceinline__ float add_bf16x2(uint32_t w, float acc) {
                                          __builtin_bit_cast(bf16x2, 0x3f803f80u), acc, false);
 }
 
+// Work-group id -> (schedule position, query head).  With the key/value heads
+// splitting evenly over the XCDs, each XCD takes its key/value heads one at a
+// time: every position of one head group (the query heads sharing that K and V)
+// before the next group, the group's query heads next to each other, so the
+// work-groups in flight on one XCD read one head's K and V and share them in
+// the XCD's L2.  Otherwise position-major.
+__device__ __forceinline__ void dense_slot(int b, int Hq, int grp, int NBR, int kv_major, int &pos,
+                                           int &h) {
+  if (kv_major) {
+    const int x = b % kQkXcds, k = b / kQkXcds;
+    const int r = k % grp, k2 = k / grp;
+    pos = k2 % NBR;
+    h = (x + kQkXcds * (k2 / NBR)) * grp + r;
+  } else {
+    pos = b / Hq;
+    h = b % Hq;
+  }
+}
+
 template <int D, bool F32>
 __global__ __launch_bounds__(kDenseQB * 2) __attribute__((amdgpu_waves_per_eu(2))) void k_dense(
     const void *__restrict__ qv, const void *__restrict__ kv, const uint16_t *__restrict__ vt,
     int64_t T, int32_t Hq, int32_t grp, int32_t NBR, const RowInfo *__restrict__ rows,
-    const int32_t *__restrict__ sched, float scale2, BiasArgs bias, float *__restrict__ o) {
+    const int32_t *__restrict__ sched, float scale2, BiasArgs bias, float *__restrict__ o,
+    int32_t kv_major) {
   using DC = DenseCfg<D, F32>;
   using C = typename DC::C;
   constexpr int QB = DC::QB, KB = DC::KB, NT = DC::NT;
@@ -128,7 +148,8 @@ __global__ __launch_bounds__(kDenseQB * 2) __attribute__((amdgpu_waves_per_eu(2)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int m = lane & 31, hl = lane >> 5;
-  const int pos = blockIdx.x / Hq, h = blockIdx.x % Hq;
+  int pos, h;
+  dense_slot(blockIdx.x, Hq, grp, NBR, kv_major, pos, h);
   const int g = h / grp;
   const int gr = sched[pos];
   const RowInfo ri = rows[gr];
@@ -391,7 +412,8 @@ static mf_status launch_dense(hipStream_t s, const void *q, const void *k, const
   if (DenseCfg<D, F32>::SMEM > 160 * 1024) return MF_ERR_UNSUPPORTED;
   hipLaunchKernelGGL((k_dense<D, F32>), dim3((unsigned)((int64_t)g.NBR * Hq)), dim3(kDenseQB * 2),
                      0, s, q, k, at<uint16_t>(ws, w.vt), g.T, Hq, Hq / Hkv, g.NBR,
-                     at<RowInfo>(ws, w.rt.rows), at<int32_t>(ws, w.rt.sched), scale2, ba, o);
+                     at<RowInfo>(ws, w.rt.rows), at<int32_t>(ws, w.rt.sched), scale2, ba, o,
+                     (int32_t)(Hkv % kQkXcds == 0));
   return hip_status();
 }
 

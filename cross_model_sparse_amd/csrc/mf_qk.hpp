@@ -15,6 +15,8 @@
 
 namespace mf {
 
+constexpr int kQkXcds = 8;  // XCDs; consecutive work-group ids go to them in turn
+
 template <int B, int D, bool F32>
 struct QKCfg {
   static constexpr int NW = B / 32;                 // waves per work-group
