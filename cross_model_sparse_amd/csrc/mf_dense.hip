@@ -115,25 +115,6 @@ __device__ __forceinline__ float add_bf16x2(uint32_t w, float acc) {
                                          __builtin_bit_cast(bf16x2, 0x3f803f80u), acc, false);
 }
 
-// Work-group id -> (schedule position, query head).  With the key/value heads
-// splitting evenly over the XCDs, each XCD takes its key/value heads one at a
-// time: every position of one head group (the query heads sharing that K and V)
-// before the next group, the group's query heads next to each other, so the
-// work-groups in flight on one XCD read one head's K and V and share them in
-// the XCD's L2.  Otherwise position-major.
-__device__ __forceinline__ void dense_slot(int b, int Hq, int grp, int NBR, int kv_major, int &pos,
-                                           int &h) {
-  if (kv_major) {
-    const int x = b % kQkXcds, k = b / kQkXcds;
-    const int r = k % grp, k2 = k / grp;
-    pos = k2 % NBR;
-    h = (x + kQkXcds * (k2 / NBR)) * grp + r;
-  } else {
-    pos = b / Hq;
-    h = b % Hq;
-  }
-}
-
 template <int D, bool F32>
 __global__ __launch_bounds__(kDenseQB * 2) __attribute__((amdgpu_waves_per_eu(2))) void k_dense(
     const void *__restrict__ qv, const void *__restrict__ kv, const uint16_t *__restrict__ vt,
@@ -149,7 +130,7 @@ __global__ __launch_bounds__(kDenseQB * 2) __attribute__((amdgpu_waves_per_eu(2)
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int m = lane & 31, hl = lane >> 5;
   int pos, h;
-  dense_slot(blockIdx.x, Hq, grp, NBR, kv_major, pos, h);
+  kv_major_slot(blockIdx.x, Hq, grp, NBR, kv_major, pos, h);
   const int g = h / grp;
   const int gr = sched[pos];
   const RowInfo ri = rows[gr];

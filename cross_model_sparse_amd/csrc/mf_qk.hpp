@@ -17,6 +17,27 @@ namespace mf {
 
 constexpr int kQkXcds = 8;  // XCDs; consecutive work-group ids go to them in turn
 
+// Work-group id -> (schedule position, query head) for kernels with one
+// work-group per (query block, query head) that read the K (and V) of head
+// h / grp.  With those key/value heads splitting evenly over the XCDs
+// (kv_major), each XCD takes its key/value heads one at a time: every position
+// of one head group (the query heads sharing that K) before the next group,
+// the group's query heads next to each other, so the work-groups in flight on
+// one XCD read one head's K and share it in the XCD's L2.  Otherwise
+// position-major.
+__device__ __forceinline__ void kv_major_slot(int b, int Hq, int grp, int NBR, int kv_major,
+                                              int &pos, int &h) {
+  if (kv_major) {
+    const int x = b % kQkXcds, k = b / kQkXcds;
+    const int r = k % grp, k2 = k / grp;
+    pos = k2 % NBR;
+    h = (x + kQkXcds * (k2 / NBR)) * grp + r;
+  } else {
+    pos = b / Hq;
+    h = b % Hq;
+  }
+}
+
 template <int B, int D, bool F32>
 struct QKCfg {
   static constexpr int NW = B / 32;                 // waves per work-group
