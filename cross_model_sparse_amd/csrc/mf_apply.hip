@@ -349,17 +349,6 @@ __device__ __forceinline__ void xcd_map(int Ht, int &pos, int &t) {
   pos = round * kXcds + ((round & 1) ? (kXcds - 1 - x) : x);
 }
 
-// acc += c * (bf16 pair) for both halves of a packed word, one dot2 each:
-// dot2([lo, hi], [c, 0]) = c * lo and dot2([lo, hi], [0, c]) = c * hi, fp32
-// accumulate; the coefficient is held in bf16.
-__device__ __forceinline__ void mix_word(float &even, float &odd, uint32_t w, uint32_t c_lo,
-                                         uint32_t c_hi) {
-  even = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w),
-                                         __builtin_bit_cast(bf16x2, c_lo), even, false);
-  odd = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w),
-                                        __builtin_bit_cast(bf16x2, c_hi), odd, false);
-}
-
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glob_void;
 // global-memory views for loads from a wave-uniform base (selects the
@@ -499,16 +488,8 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(4))) void
   row_maps_fill<B, C::NT>(mp, ns, row_ptr, col_idx, capacity, kept_mass, T, NBR, grm, tok0, I, L,
                           (n + 31) / 32, renorm, tid);
 
-  // coefficients of this lane's two rows, [c, 0] and [0, c] bf16 pairs (zero
-  // for missing sources)
   constexpr int RG = C::RG;
-  uint32_t clo[RG][4];
-#pragma unroll
-  for (int h = 0; h < RG; ++h)
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      clo[h][u] = u < ns ? pack_bf16x2(mp.coef[u * B + wave * 16 * RG + 16 * h + m16], 0.f) & 0xffffu
-                         : 0u;
+  static_assert(RG == 1, "one row group per wave: the coefficients below are the lane's row's");
 
   const int nblk = build_block_list<C::NT>(mp, ns, n, capacity, tid);
 
@@ -576,7 +557,8 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(4))) void
 #pragma unroll
     for (int nb = 0; nb < D / 16; ++nb) acc[h][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // fp8: coefficients in fp32, scaled per chunk by the tile's block scale
+  // coefficients of the lane's row in fp32 (zero for missing sources); fp8
+  // tiles scale them per chunk by the tile's block scale
   float cf[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) cf[u] = u < ns ? mp.coef[u * B + wave * 16 * RG + m16] : 0.f;
@@ -636,11 +618,14 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(4))) void
 #pragma unroll
               for (int e = 0; e < 8; ++e) mx[e] = 0.f;
               if constexpr (!FP8) {
+                // bf16 values widened exactly, fp32 FMAs
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
 #pragma unroll
-                  for (int e = 0; e < 4; ++e)
-                    mix_word(mx[2 * e], mx[2 * e + 1], cr[h][u][e], clo[h][u], clo[h][u] << 16);
+                  for (int e = 0; e < 4; ++e) {
+                    mx[2 * e] = fmaf(cf[u], __uint_as_float(cr[h][u][e] << 16), mx[2 * e]);
+                    mx[2 * e + 1] = fmaf(cf[u], __uint_as_float(cr[h][u][e] & 0xffff0000u), mx[2 * e + 1]);
+                  }
               } else {
                 // code_value * 2^(scale byte - 127), the scale folded into c
 #pragma unroll
@@ -703,11 +688,11 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(4))) void
 // One work-group per (query block, group of G consecutive targets); one wave
 // per 16 query rows, for all G targets.  Every source tile chunk (16 rows x 32
 // keys, one 1 KB fragment block) is loaded once per work-group and mixed into
-// the G translated rows.  Sources go two at a time: v_perm_b32 pairs their e-th
-// elements into one bf16 pair [P1[e], P2[e]], and one v_dot2 with the
-// coefficient pair [c1, c2] adds both products, so every instruction does two
-// multiply-adds and the pairing is shared by the G targets.  The coefficients
-// are c = W[t,h] / kmass_h[i] (bf16).
+// the G translated rows.  Each stored value is widened to fp32 exactly, once
+// for the G targets, and every target adds it times its fp32 coefficient
+// c = W[t,h] / kmass_h[i] with one FMA, so that the translated tile is rounded
+// once, to bf16, as the MFMA operand.  (Mixed-sign weights cancel: a bf16
+// coefficient's rounding would grow relative to the mixed value.)
 //
 // Per key block of the union, the block's V tiles (one per distinct V head of
 // the group) load into LDS while the first 32-key chunk is mixed; a wait for
@@ -734,9 +719,9 @@ struct ApplyMixCfg {
 // (nvh = most distinct V heads in one target group), then src[Hs] int32,
 // rbase[Hs] int64, wtab[Hs4][4] fp32 (weight of each source for each target of
 // the group), bm[Hs][nbw], pc[Hs][nbw], uni[nbw], rtab[Hs4][B] fp32 (1 / kept
-// mass of each row, 0 where none), ctab[Hs4 / 2][B][4] if used (bf16 maps: each
-// source pair's coefficient pair W[t,h] / kmass_h[i] per row and target, formed
-// once instead of in every chunk), blist[nbw * 32], counters.  The weight and
+// mass of each row, 0 where none), ctab[Hs4][B][4] fp32 if used (bf16 maps: each
+// source's coefficient W[t,h] / kmass_h[i] per row and target, formed once
+// instead of in every chunk), blist[nbw * 32], counters.  The weight and
 // coefficient tables run to Hs4 = Hs rounded up to a whole source batch, zero
 // past the sources, so the mixing loop reads them without bounds tests.
 inline size_t mix_smem(int B, int D, int Hs, int nbw, int nvh, bool ctab) {
@@ -745,7 +730,7 @@ inline size_t mix_smem(int B, int D, int Hs, int nbw, int nvh, bool ctab) {
   s += (size_t)Hs * (4 + 8) + Hs4 * 16;
   s += (size_t)Hs * nbw * 8 + (size_t)nbw * 4;
   s += Hs4 * B * 4;
-  if (ctab) s += Hs4 / 2 * B * 16;
+  if (ctab) s += Hs4 * B * 16;
   s += (size_t)nbw * 32 * 4;
   s += 64 + 64;
   return s;
@@ -776,7 +761,7 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(2))) void
   const int o_uni = o_pc + Hs * nbw * 4;
   const int o_rt = o_uni + nbw * 4;
   const int o_ct = o_rt + Hs4 * B * 4;
-  const int o_bl = o_ct + (CT ? Hs4 / 2 * B * 16 : 0);
+  const int o_bl = o_ct + (CT ? Hs4 * B * 16 : 0);
   const int o_misc = o_bl + nbw * 32 * 4;
   int32_t *src = reinterpret_cast<int32_t *>(smem + o_src);
   int64_t *rbase = reinterpret_cast<int64_t *>(smem + o_rbase);
@@ -785,7 +770,7 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(2))) void
   int32_t *pc = reinterpret_cast<int32_t *>(smem + o_pc);
   uint32_t *uni = reinterpret_cast<uint32_t *>(smem + o_uni);
   float *rtab = reinterpret_cast<float *>(smem + o_rt);
-  u32x4 *ctab = reinterpret_cast<u32x4 *>(smem + o_ct);
+  f32x4 *ctab = reinterpret_cast<f32x4 *>(smem + o_ct);
   int32_t *blist = reinterpret_cast<int32_t *>(smem + o_bl);
   int32_t *misc = reinterpret_cast<int32_t *>(smem + o_misc);  // [0] ns, [1..G] active
 
@@ -881,16 +866,14 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(2))) void
   }
   __syncthreads();
   if constexpr (CT) {
-    // coefficient pairs [c(2pq), c(2pq + 1)] of every source pair, row and
-    // target, in bf16 for v_dot2 (a missing second source: 0)
-    for (int idx = tid; idx < ns4 / 2 * B; idx += C::NT) {
-      const int pq = idx / B, il = idx % B;
-      const int u1 = 2 * pq, u2 = u1 + 1;
-      const float ra = rtab[u1 * B + il], rb = rtab[u2 * B + il];
-      u32x4 cq = u32x4{0u, 0u, 0u, 0u};
+    // fp32 coefficients of every source, row and target (0 past the sources)
+    for (int idx = tid; idx < ns4 * B; idx += C::NT) {
+      const int u = idx / B, il = idx % B;
+      const float r = rtab[u * B + il];
+      f32x4 cq = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int g = 0; g < G; ++g) cq[g] = pack_bf16x2(wtab[u1 * 4 + g] * ra, wtab[u2 * 4 + g] * rb);
-      ctab[pq * B + il] = cq;
+      for (int g = 0; g < G; ++g) cq[g] = wtab[u * 4 + g] * r;
+      ctab[u * B + il] = cq;
     }
     __syncthreads();
   }
@@ -999,62 +982,52 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(2))) void
         }
       }
     };
-    // mix one batch of SB sources (u0 ..) into mx, two sources per v_dot2
+    // mix one batch of SB sources (u0 ..) into mx in fp32: each stored tile
+    // value widened exactly (bf16 by a shift or mask, E4M3 by v_cvt_pk_f32_fp8)
+    // and multiplied with its fp32 coefficient W[t,h] / kmass_h[i], so the only
+    // rounding of the translated tile is the one to bf16 below
     auto mix_batch = [&](float (&mx)[G][8], const u32x4 (&cur)[SB], const uint32_t (&scur)[SB], int u0) {
 #pragma unroll
-      for (int pr = 0; pr < SB / 2; ++pr) {
-        const int u1 = u0 + 2 * pr, u2 = u1 + 1;
-        uint32_t cp[G];
+      for (int b = 0; b < SB; ++b) {
+        const int u = u0 + b;
+        float cf[G];
         if constexpr (CT) {
-          // the pair's coefficients from the table (zero past the sources)
-          const u32x4 cq = ctab[(u1 / 2) * B + r0];
+          // the source's coefficients from the table (zero past the sources)
+          const f32x4 cq = ctab[u * B + r0];
 #pragma unroll
-          for (int g = 0; g < G; ++g) cp[g] = cq[g];
+          for (int g = 0; g < G; ++g) cf[g] = cq[g];
         } else {
-          float ra = rtab[u1 * B + r0];
-          float rb = rtab[u2 * B + r0];
+          float r = rtab[u * B + r0];
           if constexpr (FP8) {
-            // the block scales 2^(byte - 127) folded into the coefficients
-            ra = __builtin_amdgcn_ldexpf(ra, (int)scur[2 * pr] - 127);
-            rb = __builtin_amdgcn_ldexpf(rb, (int)scur[2 * pr + 1] - 127);
+            // the block scale 2^(byte - 127) folded into the coefficients
+            r = __builtin_amdgcn_ldexpf(r, (int)scur[b] - 127);
           }
 #pragma unroll
-          for (int g = 0; g < G; ++g) cp[g] = pack_bf16x2(wtab[u1 * 4 + g] * ra, wtab[u2 * 4 + g] * rb);
+          for (int g = 0; g < G; ++g) cf[g] = wtab[u * 4 + g] * r;
         }
+        float x[8];
         if constexpr (!FP8) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const uint32_t lo = __builtin_amdgcn_perm(cur[2 * pr + 1][e], cur[2 * pr][e], 0x05040100u);
-            const uint32_t hi = __builtin_amdgcn_perm(cur[2 * pr + 1][e], cur[2 * pr][e], 0x07060302u);
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-              mx[g][2 * e] = __builtin_amdgcn_fdot2_f32_bf16(
-                  __builtin_bit_cast(bf16x2, lo), __builtin_bit_cast(bf16x2, cp[g]), mx[g][2 * e], false);
-              mx[g][2 * e + 1] = __builtin_amdgcn_fdot2_f32_bf16(
-                  __builtin_bit_cast(bf16x2, hi), __builtin_bit_cast(bf16x2, cp[g]), mx[g][2 * e + 1], false);
-            }
+            x[2 * e] = __uint_as_float(cur[b][e] << 16);
+            x[2 * e + 1] = __uint_as_float(cur[b][e] & 0xffff0000u);
           }
         } else {
-          // byte pairs [P1[e], P2[e]] of the two sources' codes, then E4M3 ->
-          // bf16 (exact: 3 mantissa bits, and the scale 1 changes nothing)
+          // code byte k of word w is element 4 w + k
 #pragma unroll
-          for (int w = 0; w < 2; ++w)
-#pragma unroll
-            for (int hw = 0; hw < 2; ++hw) {
-              const uint32_t pairs = __builtin_amdgcn_perm(
-                  cur[2 * pr + 1][w], cur[2 * pr][w], hw ? 0x07030602u : 0x05010400u);
-              const bf16x2 pv[2] = {__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(pairs, 1.0f, false),
-                                    __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(pairs, 1.0f, true)};
-#pragma unroll
-              for (int k = 0; k < 2; ++k) {
-                const int e = 4 * w + 2 * hw + k;
-#pragma unroll
-                for (int g = 0; g < G; ++g)
-                  mx[g][e] = __builtin_amdgcn_fdot2_f32_bf16(pv[k], __builtin_bit_cast(bf16x2, cp[g]),
-                                                             mx[g][e], false);
-              }
-            }
+          for (int w = 0; w < 2; ++w) {
+            const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)cur[b][w], false);
+            const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)cur[b][w], true);
+            x[4 * w + 0] = lo[0];
+            x[4 * w + 1] = lo[1];
+            x[4 * w + 2] = hi[0];
+            x[4 * w + 3] = hi[1];
+          }
         }
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) mx[g][e] = fmaf(cf[g], x[e], mx[g][e]);
       }
     };
     // chunk kc mixed: round to bf16 and multiply with V on MFMA

@@ -60,10 +60,12 @@ def test_workload1_full(gpu):
     (3, [777], dict(Hs=6, Ht=8, Hkv=2)),
     (4, [1100], dict(Hs=8, Ht=16, Hkv=16)),
     (5, [300, 520, 64, 1, 129, 0, 700], dict(Hs=4, Ht=4, Hkv=4)),
+    (5, [300, 520, 64, 1, 129, 0, 700], dict(Hs=8, Ht=8, Hkv=8)),
 ])
 def test_small_variants(gpu, idx, lens, kw):
     """Each workload's generator at oracle-sized lengths with ragged tails, an empty
-    and a one-token sequence (multi-turn), GQA and sparse Dirichlet W."""
+    and a one-token sequence (multi-turn), GQA and sparse Dirichlet W.  Eight source
+    heads over several sequences take the compressor's head-major work-group order."""
     full_case(wlmod.small_variant(idx, lens, **kw), gpu)
 
 
@@ -322,8 +324,12 @@ def test_full_size_parity(gpu, idx):
 
 @pytest.mark.parametrize("lens,Hq,Hkv,d,dt", [([256], 2, 2, 64, "fp32"), ([500, 0, 37], 8, 2, 128, "bf16"),
                                              ([1000], 4, 4, 64, "bf16"), ([4500, 129], 4, 2, 128, "bf16"),
-                                             ([700, 300], 2, 1, 128, "fp32")])
+                                             ([700, 300], 2, 1, 128, "fp32"),
+                                             ([700, 0, 333, 129], 16, 8, 128, "bf16"),
+                                             ([520, 77], 8, 8, 64, "fp32")])
 def test_dense_attention(gpu, lens, Hq, Hkv, d, dt):
+    """Dense attention against the oracle; eight key/value heads (the last two
+    cases) take the key/value-head-major work-group order."""
     spec = wlmod.Spec("dense", tuple(lens), Hq, Hq, Hkv, d, 64, 1.0, dt, 100, "gauss", w_var=1.0, seed=55)
     wl = wlmod.make_workload(spec)
     q, _ = to_dev_qk(wl, gpu)
