@@ -744,7 +744,7 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(2))) void
     const uint16_t *__restrict__ vt, const RowInfo *__restrict__ rows,
     const int32_t *__restrict__ sched, int32_t nrows, int32_t nbw, int64_t capacity,
     int32_t renorm, float *__restrict__ o, const int32_t *__restrict__ row_alias, int32_t nvmax,
-    const char *__restrict__ zbuf) {
+    const char *__restrict__ zbuf, const int32_t *__restrict__ mix_flag) {
   using C = ApplyMixCfg<B, D, FMT>;
   constexpr int G = C::G, KC = C::KC, SB = C::SB, NP = C::NP;
   constexpr bool FP8 = FMT == MF_TILE_MXFP8;
@@ -774,6 +774,8 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(2))) void
   int32_t *blist = reinterpret_cast<int32_t *>(smem + o_bl);
   int32_t *misc = reinterpret_cast<int32_t *>(smem + o_misc);  // [0] ns, [1..G] active
 
+  // no target with more than four sources (the pairing pass found none): done
+  if (mix_flag && *mix_flag == 0) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m16 = lane & 15, kg = lane >> 4;
   const int ngrp = (Ht + G - 1) / G;
@@ -1866,7 +1868,8 @@ static mf_status launch_apply_fmt(hipStream_t s, const mf_bsr_map *map, const fl
                        smem_mix, s, map->row_ptr, map->col_idx, tiles, map->kept_mass,
                        map->num_heads, g.NBR, g.T, W, Ht, Ht / Hkv, at<uint16_t>(ws, w.vt),
                        at<RowInfo>(ws, w.rt.rows), sched, nrows, nbw, map->capacity_tiles, renorm,
-                       o, map->row_alias, nvmax, at<char>(ws, w.vzero));
+                       o, map->row_alias, nvmax, at<char>(ws, w.vzero),
+                       FMT == MF_TILE_BF16 ? at<int32_t>(ws, w.gtab) + kMixFlag : nullptr);
   };
   if (use_ct)
     launch_mix(std::integral_constant<bool, FMT == MF_TILE_BF16>{});
