@@ -282,27 +282,19 @@ __global__ __launch_bounds__(1024) void k_offsets(const int32_t *__restrict__ co
                                                   int64_t capacity, int64_t *__restrict__ row_ptr,
                                                   int64_t *__restrict__ nnz,
                                                   int32_t *__restrict__ status) {
-  __shared__ int64_t ts[1024];
-  const int tid = threadIdx.x, nt = blockDim.x;
+  __shared__ int64_t wsum[16];
+  const int tid = threadIdx.x, nt = blockDim.x;  // nt == 1024
   const int64_t per = (R + nt - 1) / nt;
   const int64_t a = min(R, (int64_t)tid * per), b = min(R, a + per);
   int64_t s = 0;
   for (int64_t i = a; i < b; ++i) s += counts[i];
-  ts[tid] = s;
-  __syncthreads();
-  if (tid == 0) {
-    int64_t run = 0;
-    for (int i = 0; i < nt; ++i) {
-      const int64_t x = ts[i];
-      ts[i] = run;
-      run += x;
-    }
-    row_ptr[R] = run;
-    *nnz = run;
-    *status = run > capacity ? (int32_t)MF_ERR_CAPACITY : (int32_t)MF_OK;
+  const int64_t incl = block_scan_incl(s, wsum);
+  if (tid == nt - 1) {
+    row_ptr[R] = incl;
+    *nnz = incl;
+    *status = incl > capacity ? (int32_t)MF_ERR_CAPACITY : (int32_t)MF_OK;
   }
-  __syncthreads();
-  int64_t run = ts[tid];
+  int64_t run = incl - s;
   for (int64_t i = a; i < b; ++i) {
     row_ptr[i] = run;
     run += counts[i];

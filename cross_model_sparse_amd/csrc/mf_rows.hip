@@ -6,24 +6,6 @@
 
 namespace mf {
 
-// Inclusive prefix sum of one value per thread over a 1024-thread block: a
-// shuffle scan inside each wave, then the wave totals.  `wsum` holds 16
-// entries of LDS; every thread must call it.
-__device__ __forceinline__ int64_t block_scan_incl(int64_t v, int64_t *wsum) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int64_t u = __shfl_up(v, d, 64);
-    if (lane >= d) v += u;
-  }
-  if (lane == 63) wsum[wave] = v;
-  __syncthreads();
-  int64_t before = 0;
-  for (int w = 0; w < wave; ++w) before += wsum[w];
-  __syncthreads();  // wsum free for the next scan
-  return v + before;
-}
-
 __global__ __launch_bounds__(1024) void k_rowtable(const int32_t *__restrict__ cu, int32_t nseq,
                                                    int32_t B, int32_t maxnb,
                                                    RowInfo *__restrict__ rows,
