@@ -250,6 +250,10 @@ size_t mf_apply_workspace_bytes(int32_t Hkv, const int32_t *cu_seqlens_host, int
  * cached map: O_h = renorm(A_hat_h) V_h (AttnCache guide, architecture
  * figure, cache-hit path).
  *
+ * Precision: each translated tile is mixed in fp32 (the stored tile values
+ * widened exactly, fp32 coefficients W[t,h] / kept_mass_h[i]), rounded once to
+ * bf16, and multiplied with V on bf16 MFMA with fp32 accumulation.
+ *
  * map         host struct filled by mf_compress_topp; read only.
  * W           [Ht][map->num_heads] fp32, any sign; zero entries are skipped.
  * v           [Hkv][T][d] bf16 bit patterns, T = map->total_tokens.
