@@ -210,22 +210,27 @@ __global__ __launch_bounds__(B * 2) __attribute__((amdgpu_waves_per_eu(SelectCfg
   const int c0 = min(n, tid * per), c1 = min(n, c0 + per);
   double loc = 0.0;
   for (int c = c0; c < c1; ++c) loc += (double)__uint_as_float((uint32_t)(keys[c] >> 32));
-  tsum[tid] = loc;
-  __syncthreads();
-  if (tid == 0) {
-    double run = 0.0;
-    for (int t = 0; t < C::NT; ++t) {
-      const double x = tsum[t];
-      tsum[t] = run;
-      run += x;
-    }
-    tsum[C::NT] = run;
+  // thread prefixes: a shuffle scan inside each wave, then the wave totals
+  double incl = loc;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const double u = __shfl_up(incl, d, kWave);
+    if (lane >= d) incl += u;
   }
+  double excl = __shfl_up(incl, 1, kWave);
+  if (lane == 0) excl = 0.0;
+  if (lane == kWave - 1) tsum[wave] = incl;
   __syncthreads();
-  const double total = tsum[C::NT];
+  double total = 0.0;
+#pragma unroll
+  for (int w = 0; w < C::NW; ++w) {
+    const double x = tsum[w];
+    if (w < wave) excl += x;
+    total += x;
+  }
   const double target = p * total;
   int below = 0;
-  double run = tsum[tid];
+  double run = excl;
   for (int c = c0; c < c1; ++c) {
     run += (double)__uint_as_float((uint32_t)(keys[c] >> 32));
     below += (run < target) ? 1 : 0;
