@@ -210,9 +210,11 @@ def test_dense_mixing_exact_coefficients(gpu, idx, lens, kw, fmt):
     """Dense mixing (more than four sources per target, mixed-sign Gaussian W,
     where the mixed value can be much smaller than its terms) keeps each
     coefficient W[t,h] / kmass_h[i] in fp32.  Against the retrieval on the stored
-    tile values with exact coefficients, the GPU may differ only by the translated
-    tile's own rounding to bf16 (2^-8 relative at most); and it must be closer to
-    it than a bf16 rounding of the coefficients alone would be."""
+    tile values with exact coefficients, the GPU differs by the translated tile's
+    own rounding to bf16 (2^-9 per element, which the sum over keys can grow
+    where its mixed-sign terms cancel; 1.8e-3 to 3.3e-3 on these cases, held
+    under 2^-8), and it must be closer to that retrieval than a bf16 rounding of
+    the coefficients alone would put it."""
     wl = wlmod.small_variant(idx, lens, **kw)
     B = wl.spec.B
     assert (np.count_nonzero(wl.W, axis=1) > 4).all()
